@@ -1,0 +1,359 @@
+"""Plain fp64 CPU oracle for CoWindow Attention (CoWA).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this module.  The GPU library
+never calls it and shares no code with it: this file has its own visibility
+predicate, its own interval and tile enumeration, and a dense masked softmax.
+
+Sources (pages are cited by title and paragraph; they carry no numbered
+sections, equations or listings):
+
+  [SF] "Splitting long-range windows across KV heads beats duplicating them at
+       lower cost" (skillfed.io news, 2026-09-30).  Second paragraph: all KV
+       heads share a near-diagonal window and a prefix-sink window; the rest
+       of the causal history is cut into non-overlapping long-range intervals,
+       one per KV head; the pattern is position arithmetic only.  Paragraph
+       "What CoWA does not claim": every head applies softmax over its own
+       visible set.  Sixth paragraph: global KV-head indexing keeps the bands
+       complementary across tensor-parallel ranks.
+  [AB] "CoWindow Attention: Full Causal Coverage Is a Collective Property",
+       Abstract (newx.sg paper page; same text on the acceptodds.com ICLR 2027
+       submission page): complementary long-range windows partition the
+       remaining history and, with the shared windows, their union gives full
+       causal coverage; FullAttn is the dense comparison.
+
+Readings where the pages give no formula (each is listed in the design doc):
+
+  * Band partition.  The pages state the structure but no formula.  This
+    oracle fixes: with L = ceil((N_ctx - W) / H_kv_global) when N_ctx > W and
+    L = 0 otherwise, KV head with global index g sees keys at query-to-key
+    distance t - j in the half-open interval [W + g*L, W + (g+1)*L).
+  * Shared windows: the sink is keys j < S, the local window is distances
+    t - j < W (so W keys including the diagonal).  Both are intersected with
+    causality j <= t.
+  * A key reachable through several windows counts once (set union).
+  * GQA: query head hq uses local KV head h = hq // G with G = H_q / H_kv_local;
+    its global index is g = kv_head_offset + h.
+  * Decode: the new token's K/V are already in the cache, so the query
+    position is t = len - 1.
+  * LSE is the natural-log log-sum-exp of the scaled scores over the visible
+    set.
+
+Parity status: the visibility predicate, interval form, tile lists and the
+masked softmax are pinned by the CPU tests (hand-derived 16-token grid,
+coverage/disjointness invariants, closed-form pair counts, reductions to
+textbook dense causal softmax, closed-form band-only case, softmax identities
+checked against scipy).  Numeric O/LSE values for the benchmark workloads are
+not printed by the pages; for those the definition below plus the reductions
+above are the only pins.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+MODE_COWA = 0
+MODE_CAUSAL = 1
+
+
+@dataclass(frozen=True)
+class Pattern:
+    """Position-only pattern parameters ([SF] second paragraph; [AB] Abstract).
+
+    n_ctx: context length the band width is derived from.
+    sink: S, keys j < S are shared by every head.
+    window: W, distances t - j < W are shared by every head.
+    band: L; a value <= 0 means "derive from n_ctx, window, h_kv_global".
+    h_kv_global: number of KV heads across all tensor-parallel ranks.
+    kv_head_offset: global index of this rank's first KV head ([SF] sixth
+        paragraph: bands follow the global KV-head index).
+    mode: MODE_COWA or MODE_CAUSAL (dense causal FullAttn, [AB] Abstract).
+    """
+
+    n_ctx: int
+    sink: int
+    window: int
+    band: int = 0
+    h_kv_global: int = 1
+    kv_head_offset: int = 0
+    mode: int = MODE_COWA
+
+
+def band_length(n_ctx: int, window: int, h_kv_global: int) -> int:
+    """L = ceil((N_ctx - W) / H_kv_global) if N_ctx > W else 0 (band reading)."""
+    if n_ctx <= window:
+        return 0
+    rest = n_ctx - window
+    # integer ceiling division, written out
+    q, r = divmod(rest, h_kv_global)
+    return q + (1 if r else 0)
+
+
+def resolved_band(p: Pattern) -> int:
+    return p.band if p.band > 0 else band_length(p.n_ctx, p.window, p.h_kv_global)
+
+
+def visible(t, j, g, p: Pattern):
+    """Element predicate vis_g(t, j) (broadcasting over numpy arrays).
+
+    CoWA: j <= t and (j < S or t - j < W or W + g*L <= t - j < W + (g+1)*L).
+    Causal mode: j <= t.
+    """
+    t = np.asarray(t, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    dist = t - j
+    causal = (dist >= 0) & (j >= 0)
+    if p.mode == MODE_CAUSAL:
+        return causal
+    L = resolved_band(p)
+    in_sink = j < p.sink
+    in_local = dist < p.window
+    if L > 0:
+        lo = p.window + g * L
+        hi = p.window + (g + 1) * L
+        in_band = (dist >= lo) & (dist < hi)
+    else:
+        in_band = np.zeros(np.broadcast(t, j).shape, dtype=bool)
+    return causal & (in_sink | in_local | in_band)
+
+
+def visible_mask(n_rows: int, n_keys: int, g: int, p: Pattern) -> np.ndarray:
+    """Dense boolean [n_rows, n_keys] mask for small sizes."""
+    t = np.arange(n_rows)[:, None]
+    j = np.arange(n_keys)[None, :]
+    return np.broadcast_to(visible(t, j, g, p), (n_rows, n_keys)).copy()
+
+
+def visible_intervals(t: int, g: int, p: Pattern):
+    """Row t's visible keys as sorted, disjoint, non-adjacent [a, b) intervals.
+
+    A second, independent derivation of the same set: each window is turned
+    into a key interval and the intervals are merged.
+    """
+    if t < 0:
+        return []
+    ivs = []
+    if p.mode == MODE_CAUSAL:
+        ivs.append((0, t + 1))
+    else:
+        L = resolved_band(p)
+        if p.sink > 0:
+            ivs.append((0, min(p.sink, t + 1)))
+        ivs.append((max(0, t - p.window + 1), t + 1))
+        if L > 0:
+            # distances [W+gL, W+(g+1)L)  <=>  keys (t-W-(g+1)L, t-W-gL]
+            a = t - (p.window + (g + 1) * L) + 1
+            b = t - (p.window + g * L) + 1
+            a, b = max(a, 0), min(b, t + 1)
+            if a < b:
+                ivs.append((a, b))
+    ivs = sorted(iv for iv in ivs if iv[0] < iv[1])
+    merged = []
+    for a, b in ivs:
+        if merged and a <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], b))
+        else:
+            merged.append((a, b))
+    return merged
+
+
+def visible_count(t: int, g: int, p: Pattern) -> int:
+    return sum(b - a for a, b in visible_intervals(t, g, p))
+
+
+# --------------------------------------------------------------------------
+# Tile lists (the plan).  Tile (qi, kj) covers rows [qi*BM, (qi+1)*BM) and keys
+# [kj*BN, (kj+1)*BN).  Listed iff any element is visible, full iff all BM*BN
+# elements are visible (a tile reaching past N is therefore never full).
+# Rows of the CSR are ordered (h_local, qi); columns ascend.
+# --------------------------------------------------------------------------
+
+
+def _csr_from_counts(counts_per_head, bm, bn):
+    row_ptr = [0]
+    cols = []
+    flags = []
+    for counts in counts_per_head:
+        for qi in range(counts.shape[0]):
+            nz = np.nonzero(counts[qi])[0]
+            cols.extend(int(c) for c in nz)
+            flags.extend(1 if counts[qi, c] == bm * bn else 0 for c in nz)
+            row_ptr.append(len(cols))
+    return (np.asarray(row_ptr, dtype=np.int32), np.asarray(cols, dtype=np.int32),
+            np.asarray(flags, dtype=np.uint8))
+
+
+def tile_counts_bruteforce(n: int, g: int, p: Pattern, bm: int, bn: int) -> np.ndarray:
+    """Visible-element count per tile by materialising the element mask."""
+    nqt = -(-n // bm)
+    nkt = -(-n // bn)
+    m = np.zeros((nqt * bm, nkt * bn), dtype=bool)
+    m[:n, :n] = visible_mask(n, n, g, p)
+    return m.reshape(nqt, bm, nkt, bn).sum(axis=(1, 3)).astype(np.int64)
+
+
+def tile_counts_intervals(n: int, g: int, p: Pattern, bm: int, bn: int) -> np.ndarray:
+    """Visible-element count per tile from per-row intervals (large N).
+
+    For each query tile, a difference array over key positions counts how many
+    of its rows see each key; summing that over a key tile's BN positions
+    gives the tile's visible-element count.
+    """
+    nqt = -(-n // bm)
+    nkt = -(-n // bn)
+    counts = np.zeros((nqt, nkt), dtype=np.int64)
+    for qi in range(nqt):
+        diff = np.zeros(nkt * bn + 1, dtype=np.int64)
+        for t in range(qi * bm, min((qi + 1) * bm, n)):
+            for a, b in visible_intervals(t, g, p):
+                diff[a] += 1
+                diff[b] -= 1
+        per_key = np.cumsum(diff[:-1])
+        counts[qi] = per_key.reshape(nkt, bn).sum(axis=1)
+    return counts
+
+
+def tile_counts_intervals_fast(n: int, g: int, p: Pattern, bm: int, bn: int) -> np.ndarray:
+    """Same as tile_counts_intervals, vectorised over rows (for 32K-128K).
+
+    Each window of row t is an interval [a_t, b_t); the per-window intervals
+    are made disjoint first (sink, then band minus sink, then local minus the
+    other two) so that plain +1/-1 difference marks count each key once.
+    """
+    nqt = -(-n // bm)
+    nkt = -(-n // bn)
+    t = np.arange(n, dtype=np.int64)
+    if p.mode == MODE_CAUSAL:
+        ivs = [(np.zeros_like(t), t + 1)]
+    else:
+        L = resolved_band(p)
+        sink_b = np.minimum(p.sink, t + 1)
+        sink = (np.zeros_like(t), sink_b)
+        loc_a = np.maximum(np.maximum(0, t - p.window + 1), sink_b)
+        loc = (loc_a, np.maximum(t + 1, loc_a))
+        ivs = [sink, loc]
+        if L > 0:
+            ba = np.maximum(t - (p.window + (g + 1) * L) + 1, sink_b)
+            bb = np.minimum(t - (p.window + g * L) + 1, loc_a)
+            bb = np.maximum(bb, ba)
+            ivs.append((ba, bb))
+    counts = np.zeros((nqt, nkt), dtype=np.int64)
+    for qi in range(nqt):
+        r0, r1 = qi * bm, min((qi + 1) * bm, n)
+        diff = np.zeros(nkt * bn + 1, dtype=np.int64)
+        for a, b in ivs:
+            aa, bb = a[r0:r1], b[r0:r1]
+            keep = aa < bb
+            np.add.at(diff, aa[keep], 1)
+            np.add.at(diff, bb[keep], -1)
+        per_key = np.cumsum(diff[:-1])
+        counts[qi] = per_key.reshape(nkt, bn).sum(axis=1)
+    return counts
+
+
+def tile_lists(n: int, h_kv_local: int, p: Pattern, bm: int, bn: int, method: str = "auto"):
+    """CSR visible-tile lists for local heads 0..h_kv_local-1 (global g = offset + h)."""
+    if method == "auto":
+        method = "bruteforce" if n <= 4096 else "fast"
+    fn = {"bruteforce": tile_counts_bruteforce, "intervals": tile_counts_intervals,
+          "fast": tile_counts_intervals_fast}[method]
+    per_head = [fn(n, p.kv_head_offset + h, p, bm, bn) for h in range(h_kv_local)]
+    return _csr_from_counts(per_head, bm, bn)
+
+
+# --------------------------------------------------------------------------
+# Attention: dense masked softmax over each head's own visible set
+# ([SF] "What CoWA does not claim"), in float64.
+# --------------------------------------------------------------------------
+
+
+def _masked_softmax_rows(qrows, keys, vals, rows_t, g, p: Pattern, scale):
+    """qrows [R, d], keys/vals [J, d] (keys 0..J-1), rows_t [R] positions.
+
+    Returns O [R, d] and LSE [R] (natural log).
+    """
+    s = (qrows @ keys.T) * scale
+    mask = visible(rows_t[:, None], np.arange(keys.shape[0])[None, :], g, p)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    lsum = e.sum(axis=1)
+    lse = m + np.log(lsum)
+    w = np.exp(s - lse[:, None])
+    return w @ vals, lse
+
+
+def attention(q, k, v, p: Pattern, scale: float, rows=None, heads=None, row_block: int = 256):
+    """CoWA (or causal) prefill attention, fp64.
+
+    q [B, N, H_q, d]; k, v [B, N, H_kv_local, d] (any float dtype, widened to
+    float64).  rows: optional sorted array of query positions to compute (all
+    if None).  heads: optional list of query heads (all if None).
+    Returns O [B, len(rows), len(heads), d] and LSE [B, len(heads), len(rows)].
+    """
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    out = np.zeros((B, len(rows), len(heads), d), dtype=np.float64)
+    lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
+    for b in range(B):
+        for hi, hq in enumerate(heads):
+            h = hq // G
+            g = p.kv_head_offset + h
+            for r0 in range(0, len(rows), row_block):
+                rt = rows[r0:r0 + row_block]
+                J = int(rt.max()) + 1
+                qr = np.asarray(q[b, rt, hq], dtype=np.float64)
+                kk = np.asarray(k[b, :J, h], dtype=np.float64)
+                vv = np.asarray(v[b, :J, h], dtype=np.float64)
+                o, l_ = _masked_softmax_rows(qr, kk, vv, rt, g, p, scale)
+                out[b, r0:r0 + len(rt), hi] = o
+                lse[b, hi, r0:r0 + len(rt)] = l_
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, lens, p: Pattern, scale: float):
+    """Single-token decode, fp64: query position t_b = lens[b] - 1, keys 0..t_b.
+
+    q [B, H_q, d]; caches [B, N_max, H_kv_local, d]; lens [B].
+    Returns O [B, H_q, d] and LSE [B, H_q].
+    """
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    for b in range(B):
+        t = int(lens[b]) - 1
+        rt = np.asarray([t], dtype=np.int64)
+        for hq in range(Hq):
+            h = hq // G
+            g = p.kv_head_offset + h
+            kk = np.asarray(k_cache[b, :t + 1, h], dtype=np.float64)
+            vv = np.asarray(v_cache[b, :t + 1, h], dtype=np.float64)
+            o, l_ = _masked_softmax_rows(np.asarray(q[b, hq][None, :], dtype=np.float64),
+                                         kk, vv, rt, g, p, scale)
+            out[b, hq] = o[0]
+            lse[b, hq] = l_[0]
+    return out, lse
+
+
+def decode_visible_keys(t: int, g: int, p: Pattern) -> np.ndarray:
+    """Sorted key positions visible to a decode query at position t."""
+    parts = [np.arange(a, b) for a, b in visible_intervals(t, g, p)]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def visible_pairs(n: int, g: int, p: Pattern) -> int:
+    """Sum over rows t < n of |vis_g(t)| (element-level work of one head)."""
+    return int(sum(visible_count(t, g, p) for t in range(n)))
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,189 @@
+"""Seeded synthetic workloads for the CoWA operator (shapes, draws, bf16 rounding).
+
+This module holds the workload definitions and the random-input generators
+shared by the tests, the smoke check and the benchmark.  It contains none of
+the method's arithmetic: no visibility rule, no band derivation, no softmax.
+The band width each workload states is recorded as a plain number so that the
+tests can check the derivation against it.
+
+Inputs are drawn as float32 from numpy's PCG64 generator and rounded once to
+bfloat16 (round to nearest, ties to even).  Both the GPU path and the fp64
+oracle consume the rounded values, so parity measures kernel error, not input
+quantisation.  The 128K decode cache (two 4 GiB bf16 tensors) is drawn on the
+device with torch's seeded generator instead; the oracle then reads the rows
+it needs back to the host.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN_BITS = 0x7FC0
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN_BITS
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(to_bf16_bits(x))
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    N: int
+    H_q: int
+    H_kv: int            # KV heads held by this GPU
+    d: int
+    sink: int
+    window: int
+    h_kv_global: int
+    stated_band: int     # L as the workload definition states it
+    seed: int
+    offsets: tuple = (0,)  # global KV-head offsets to run
+    q_dist: str = "normal"       # "normal" | "rms1.5"
+    k_dist: str = "normal"       # "normal" | "peaky5pct"
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    n_max: int
+    n_ctx: int
+    H_q: int
+    H_kv: int
+    d: int
+    sink: int
+    window: int
+    h_kv_global: int
+    stated_band: int
+    seed: int
+    len_lo: int
+    len_hi: int          # inclusive
+    offsets: tuple = (0,)
+
+
+TINY = PrefillWorkload("tiny-1k", B=1, N=1024, H_q=8, H_kv=4, d=64, sink=16, window=128,
+                       h_kv_global=4, stated_band=224, seed=1)
+P8K = PrefillWorkload("prefill-8k", B=2, N=8192, H_q=32, H_kv=8, d=128, sink=64, window=1024,
+                      h_kv_global=8, stated_band=896, seed=2, k_dist="peaky5pct")
+P32K = PrefillWorkload("prefill-32k", B=1, N=32768, H_q=40, H_kv=8, d=128, sink=128,
+                       window=4096, h_kv_global=8, stated_band=3584, seed=3, q_dist="rms1.5")
+P128K = PrefillWorkload("prefill-128k-rank", B=1, N=131072, H_q=5, H_kv=1, d=128, sink=128,
+                        window=8192, h_kv_global=8, stated_band=15360, seed=4,
+                        offsets=tuple(range(8)))
+D128K = DecodeWorkload("decode-128k", B=16, n_max=131072, n_ctx=131072, H_q=40, H_kv=8, d=128,
+                       sink=128, window=8192, h_kv_global=8, stated_band=15360, seed=5,
+                       len_lo=98304, len_hi=131072)
+
+PREFILL_WORKLOADS = (TINY, P8K, P32K, P128K)
+
+
+@dataclass
+class PrefillInputs:
+    q_bits: np.ndarray   # uint16 [B, N, H_q, d]
+    k_bits: np.ndarray   # uint16 [B, N, H_kv, d]
+    v_bits: np.ndarray
+    extra: dict = field(default_factory=dict)
+
+    def q(self):
+        return bf16_bits_to_f32(self.q_bits)
+
+    def k(self):
+        return bf16_bits_to_f32(self.k_bits)
+
+    def v(self):
+        return bf16_bits_to_f32(self.v_bits)
+
+
+def prefill_inputs(w: PrefillWorkload, n_override: int | None = None) -> PrefillInputs:
+    """Q, K, V for a prefill workload (draw order: Q, K, V, then the K scaling mask).
+
+    q_dist "rms1.5": each query vector is rescaled to root-mean-square 1.5.
+    k_dist "peaky5pct": each key vector (b, j, h) is multiplied by 4 with
+    probability 0.05 (before rounding; x4 is exact in bf16).
+    """
+    N = w.N if n_override is None else n_override
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    q = rng.standard_normal((w.B, N, w.H_q, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.B, N, w.H_kv, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.B, N, w.H_kv, w.d), dtype=np.float32)
+    if w.q_dist == "rms1.5":
+        rms = np.sqrt(np.mean(q.astype(np.float64) ** 2, axis=-1, keepdims=True))
+        q = (q / rms * 1.5).astype(np.float32)
+    if w.k_dist == "peaky5pct":
+        hot = rng.random((w.B, N, w.H_kv), dtype=np.float64) < 0.05
+        k = np.where(hot[..., None], k * np.float32(4.0), k).astype(np.float32)
+    return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
+
+
+def random_prefill(seed, B, N, H_q, H_kv, d, scale_q=1.0):
+    """Generic N(0,1) inputs for edge-case tests (any shape)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, N, H_q, d), dtype=np.float32) * np.float32(scale_q)
+    k = rng.standard_normal((B, N, H_kv, d), dtype=np.float32)
+    v = rng.standard_normal((B, N, H_kv, d), dtype=np.float32)
+    return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
+
+
+def decode_lens(w: DecodeWorkload) -> np.ndarray:
+    """Cached lengths, integers uniform on [len_lo, len_hi] (drawn first)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    return rng.integers(w.len_lo, w.len_hi, endpoint=True, size=w.B).astype(np.int32)
+
+
+def decode_query(w: DecodeWorkload) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    rng.integers(w.len_lo, w.len_hi, endpoint=True, size=w.B)  # same stream position
+    return to_bf16_bits(rng.standard_normal((w.B, w.H_q, w.d), dtype=np.float32))
+
+
+def decode_cache_host(seed, B, n_max, H_kv, d, lens, poison=True):
+    """Small decode caches on the host: N(0,1) below each length, NaN at and after it."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = to_bf16_bits(rng.standard_normal((B, n_max, H_kv, d), dtype=np.float32))
+    v = to_bf16_bits(rng.standard_normal((B, n_max, H_kv, d), dtype=np.float32))
+    if poison:
+        for b in range(B):
+            k[b, int(lens[b]):] = BF16_NAN_BITS
+            v[b, int(lens[b]):] = BF16_NAN_BITS
+    return k, v
+
+
+def decode_cache_device(w: DecodeWorkload, lens: np.ndarray, device="cuda"):
+    """Full-size decode caches drawn on the device (torch seeded generator).
+
+    K and V are [B, n_max, H_kv, d] bf16, N(0,1) below each sequence's
+    length and NaN at and after it, so any read past a length shows up as NaN.
+    """
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    shape = (w.B, w.n_max, w.H_kv, w.d)
+    caches = []
+    for _ in range(2):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for b in range(w.B):  # per sequence, to bound the fp32 temporary
+            t[b].copy_(torch.randn(shape[1:], generator=gen, device=device,
+                                   dtype=torch.float32))
+            t[b, int(lens[b]):] = float("nan")
+        caches.append(t)
+    return caches[0], caches[1]
