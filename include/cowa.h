@@ -1,0 +1,166 @@
+/*
+ * cowa.h - C ABI of libcowa, a gfx950 (MI355X) implementation of CoWindow
+ * Attention (CoWA) prefill and decode.
+ *
+ * The method.  "CoWindow Attention: Full Causal Coverage Is a Collective
+ * Property" (Abstract) and "Splitting long-range windows across KV heads
+ * beats duplicating them at lower cost" (mechanism paragraph) describe causal
+ * GQA attention in which every KV head sees a shared prefix-sink window and a
+ * shared near-diagonal window, while the rest of the causal history is split
+ * into non-overlapping long-range intervals, one per KV head, so that the
+ * union over heads covers the whole causal prefix.  Each head applies softmax
+ * over its own visible set only (same news page, paragraph on what CoWA does
+ * not claim).  The pattern is computed from positions and the global KV-head
+ * index alone (news page, efficiency and tensor-parallelism paragraphs).
+ *
+ * The pages give no formula; this library fixes the band partition as:
+ *     L = ceil((n_ctx - W) / h_kv_global)   if n_ctx > W, else L = 0
+ *     vis_g(t, j) = j <= t && ( j < S || t - j < W ||
+ *                               (L > 0 && W + g*L <= t - j < W + (g+1)*L) )
+ * for query position t, key position j and global KV-head index g.  Query
+ * head hq uses local KV head h = hq / (H_q / H_kv_local) and
+ * g = kv_head_offset + h.  In COWA_MODE_CAUSAL, vis(t, j) = j <= t (the dense
+ * FullAttn comparison, Abstract).
+ *
+ * Conventions.
+ *  - Every device pointer is owned by the caller.  The library never
+ *    allocates or frees device memory and never synchronises; work is
+ *    enqueued on the given stream (a hipStream_t passed as void*, NULL for
+ *    the null stream).
+ *  - Host-side validation returns an error before anything is launched.  A
+ *    failed launch returns COWA_ERR_HIP.  Nothing throws across the ABI.
+ *  - bf16 means IEEE bfloat16 stored as 2 bytes.  Strides are in elements;
+ *    the last (head-dim) axis is always contiguous.
+ *  - The library is stateless and thread-safe.
+ */
+#ifndef COWA_H
+#define COWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COWA_OK = 0,
+  COWA_ERR_INVALID_ARG = 1,   /* a size, pointer or pattern field is invalid */
+  COWA_ERR_UNSUPPORTED = 2,   /* valid but not compiled (head dim, tile shape, group size) */
+  COWA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small */
+  COWA_ERR_PLAN_MISMATCH = 4, /* plan size does not match pattern/shape/tile */
+  COWA_ERR_HIP = 5,           /* a HIP launch failed */
+  COWA_ERR_CAPACITY = 6       /* caller's plan buffers are too small */
+} cowa_status;
+
+enum { COWA_MODE_COWA = 0, COWA_MODE_CAUSAL = 1 };
+enum { COWA_DTYPE_BF16 = 0, COWA_DTYPE_F32 = 1 };
+
+/* Position-only pattern (mechanism paragraph of the news page; Abstract).
+ *  n_ctx          context length the band width is derived from (for decode
+ *                 the configured maximum context, so the pattern is the
+ *                 same in training and inference)
+ *  sink           S >= 0: keys j < S are visible to every head
+ *  window         W >= 1: distances t - j < W are visible to every head
+ *  band           L; <= 0 means derive L from n_ctx, window, h_kv_global
+ *  h_kv_global    KV heads over all tensor-parallel ranks (>= 1)
+ *  kv_head_offset global index of this caller's first KV head (tensor
+ *                 parallelism keeps the bands complementary across ranks)
+ *  mode           COWA_MODE_COWA or COWA_MODE_CAUSAL */
+typedef struct {
+  int32_t n_ctx;
+  int32_t sink;
+  int32_t window;
+  int32_t band;
+  int32_t h_kv_global;
+  int32_t kv_head_offset;
+  int32_t mode;
+} cowa_pattern;
+
+/* Human-readable name of a status code (static storage). */
+const char* cowa_status_str(cowa_status s);
+
+/* Resolved band width L of a pattern, or -1 if the pattern is invalid. */
+int32_t cowa_band_length(const cowa_pattern* p);
+
+/* Tile shape (block_m query rows x block_n keys) that cowa_fwd requires for
+ * head dim d; COWA_ERR_UNSUPPORTED if d is not compiled (64 and 128 are). */
+cowa_status cowa_fwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n);
+
+/* ---- cowa_plan: visible-tile lists (host only, no device work) ----------
+ * For local KV heads h = 0..h_kv_local-1 (global g = kv_head_offset + h) and
+ * query tiles qi = 0..ceil(n/block_m)-1, lists the key tiles kj whose block
+ * [kj*block_n, (kj+1)*block_n) x rows [qi*block_m, (qi+1)*block_m) holds at
+ * least one visible (t, j) with t, j < n.  No router or content is involved:
+ * the lists are position arithmetic (news page, efficiency paragraph).
+ * Output is CSR in caller host memory:
+ *   row_ptr  int32[h_kv_local * nqt + 1], row r = h * nqt + qi
+ *   col      int32[nnz], ascending key-tile index within each row
+ *   flags    uint8[nnz], 1 if every (t, j) of the tile is visible (the
+ *            kernel then skips masking), 0 otherwise; a tile reaching past n
+ *            is never full.
+ * cowa_plan_size writes nnz; cowa_plan fails with COWA_ERR_CAPACITY if
+ * cap < nnz.  n is the number of query rows and of keys (self-attention). */
+cowa_status cowa_plan_size(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                           int32_t block_m, int32_t block_n, int64_t* nnz_out);
+cowa_status cowa_plan(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                      int32_t block_m, int32_t block_n,
+                      int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t cap);
+
+/* ---- cowa_fwd: prefill forward ------------------------------------------
+ * O[b,t,hq,:] = sum_{j in vis_g(t)} softmax_j(scale * q.k_j) v_j  and
+ * LSE[b,hq,t] = log sum_{j in vis_g(t)} exp(scale * q.k_j)  (natural log),
+ * i.e. a softmax over the head's own visible set (news page, paragraph on
+ * what CoWA does not claim).
+ *  plan        d_row_ptr/d_col/d_flags: device copies of cowa_plan's output
+ *              for (p, N, H_kv_local, block_m, block_n); nnz its length.
+ *              COWA_ERR_PLAN_MISMATCH if nnz differs from cowa_plan_size.
+ *  q           bf16 [B, N, H_q, d] with element strides strides[0..2] (b,t,h)
+ *  k, v        bf16 [B, N, H_kv_local, d], strides[3..5] and strides[6..8]
+ *  o           [B, N, H_q, d] of o_dtype (COWA_DTYPE_BF16 or _F32),
+ *              strides[9..11]
+ *  lse         fp32 [B, H_q, N], contiguous
+ *  d           64 or 128; H_q % H_kv_local == 0;
+ *              kv_head_offset + H_kv_local <= h_kv_global
+ *  softmax_scale  > 0 (usually 1/sqrt(d))
+ * Arithmetic: bf16 inputs, fp32 accumulation and softmax; P is rounded to
+ * bf16 before the P.V product. */
+cowa_status cowa_fwd(const cowa_pattern* p,
+                     const int32_t* d_row_ptr, const int32_t* d_col, const uint8_t* d_flags,
+                     int64_t nnz, int32_t block_m, int32_t block_n,
+                     const void* q, const void* k, const void* v,
+                     void* o, int32_t o_dtype, float* lse,
+                     int32_t B, int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
+                     const int64_t strides[12], float softmax_scale, void* stream);
+
+/* ---- cowa_decode: one query token per sequence --------------------------
+ * Sequence b's new token sits at position t_b = cache_seqlens[b] - 1 (its own
+ * K/V are already in the cache) and attends to vis_g(t_b) among cached keys
+ * 0..t_b; only those keys are read.  The same pattern as prefill is used, as
+ * the pages require the pattern to be identical in training and inference
+ * (Abstract).  The work is split over chunks of the visible keys of each
+ * (b, KV head); a second kernel merges the chunks by their log-sum-exp.
+ *  q              bf16 [B, H_q, d], strides[0..1] (b, h)
+ *  k_cache,v_cache bf16 [B, n_max, H_kv_local, d], strides[2..4], [5..7] (b,s,h)
+ *  cache_seqlens  device int32[B], each in [1, n_max] (not checked on the
+ *                 host; the kernels clamp to that range)
+ *  o              [B, H_q, d] of o_dtype, strides[8..9] (b, h)
+ *  lse            fp32 [B, H_q], contiguous
+ *  workspace      device scratch of at least cowa_decode_workspace_size bytes
+ *                 (256-byte aligned), else COWA_ERR_WORKSPACE
+ *  H_q / H_kv_local must be <= 8 (COWA_ERR_UNSUPPORTED otherwise). */
+cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,
+                                       int32_t H_kv_local, int32_t d, int32_t n_max,
+                                       size_t* bytes);
+cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_seqlens,
+                        void* o, int32_t o_dtype, float* lse,
+                        int32_t B, int32_t H_q, int32_t H_kv_local, int32_t d, int32_t n_max,
+                        const int64_t strides[10], float softmax_scale,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COWA_H */

@@ -1,0 +1,206 @@
+"""ctypes binding of libcowa (include/cowa.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU (torch supplies device memory and streams); the work
+itself runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, load() raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcowa.so")
+
+COWA_OK = 0
+COWA_ERR_INVALID_ARG = 1
+COWA_ERR_UNSUPPORTED = 2
+COWA_ERR_WORKSPACE = 3
+COWA_ERR_PLAN_MISMATCH = 4
+COWA_ERR_HIP = 5
+COWA_ERR_CAPACITY = 6
+COWA_MODE_COWA = 0
+COWA_MODE_CAUSAL = 1
+COWA_DTYPE_BF16 = 0
+COWA_DTYPE_F32 = 1
+
+EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa_plan_size",
+            "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode")
+
+
+class CowaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {cowa_status_str(status)} (status {status})")
+
+
+class cowa_pattern(ctypes.Structure):
+    _fields_ = [("n_ctx", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("band", ctypes.c_int32), ("h_kv_global", ctypes.c_int32),
+                ("kv_head_offset", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+
+def make_pattern(n_ctx, sink, window, band=0, h_kv_global=1, kv_head_offset=0,
+                 mode=COWA_MODE_COWA) -> cowa_pattern:
+    return cowa_pattern(n_ctx, sink, window, band, h_kv_global, kv_head_offset, mode)
+
+
+_lib = None
+
+
+def load():
+    """Load libcowa.so from the package directory (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libcowa.so not built at {LIB_PATH}; run "
+                           "python -m structured_sparse_attention_cowa_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    pat = P(cowa_pattern)
+    lib.cowa_status_str.restype = ctypes.c_char_p
+    lib.cowa_status_str.argtypes = [ctypes.c_int]
+    lib.cowa_band_length.restype = i32
+    lib.cowa_band_length.argtypes = [pat]
+    lib.cowa_fwd_block_sizes.restype = ctypes.c_int
+    lib.cowa_fwd_block_sizes.argtypes = [i32, P(i32), P(i32)]
+    lib.cowa_plan_size.restype = ctypes.c_int
+    lib.cowa_plan_size.argtypes = [pat, i32, i32, i32, i32, P(i64)]
+    lib.cowa_plan.restype = ctypes.c_int
+    lib.cowa_plan.argtypes = [pat, i32, i32, i32, i32, vp, vp, vp, i64]
+    lib.cowa_fwd.restype = ctypes.c_int
+    lib.cowa_fwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp,
+                             i32, i32, i32, i32, i32, P(i64), f32, vp]
+    lib.cowa_decode_workspace_size.restype = ctypes.c_int
+    lib.cowa_decode_workspace_size.argtypes = [pat, i32, i32, i32, i32, i32, P(ctypes.c_size_t)]
+    lib.cowa_decode.restype = ctypes.c_int
+    lib.cowa_decode.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                P(i64), f32, vp, ctypes.c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != COWA_OK:
+        raise CowaError(st, where)
+
+
+def cowa_status_str(status: int) -> str:
+    return load().cowa_status_str(int(status)).decode()
+
+
+def cowa_band_length(p: cowa_pattern) -> int:
+    return int(load().cowa_band_length(ctypes.byref(p)))
+
+
+def cowa_fwd_block_sizes(d: int):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().cowa_fwd_block_sizes(d, ctypes.byref(bm), ctypes.byref(bn)),
+           "cowa_fwd_block_sizes")
+    return bm.value, bn.value
+
+
+def cowa_plan_size(p: cowa_pattern, n: int, h_kv_local: int, block_m: int, block_n: int) -> int:
+    nnz = ctypes.c_int64()
+    _check(load().cowa_plan_size(ctypes.byref(p), n, h_kv_local, block_m, block_n,
+                                 ctypes.byref(nnz)), "cowa_plan_size")
+    return nnz.value
+
+
+def cowa_plan(p: cowa_pattern, n: int, h_kv_local: int, block_m: int, block_n: int):
+    """Returns (row_ptr int32, col int32, flags uint8) host arrays."""
+    nnz = cowa_plan_size(p, n, h_kv_local, block_m, block_n)
+    nqt = -(-n // block_m)
+    row_ptr = np.zeros(h_kv_local * nqt + 1, dtype=np.int32)
+    col = np.zeros(max(nnz, 1), dtype=np.int32)
+    flags = np.zeros(max(nnz, 1), dtype=np.uint8)
+    _check(load().cowa_plan(ctypes.byref(p), n, h_kv_local, block_m, block_n,
+                            row_ptr.ctypes.data, col.ctypes.data, flags.ctypes.data, nnz),
+           "cowa_plan")
+    return row_ptr, col[:nnz], flags[:nnz]
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _strides(t, ndim_keep):
+    assert t.stride(-1) == 1, "last (head-dim) axis must be contiguous"
+    return list(t.stride()[:ndim_keep])
+
+
+def _o_dtype(o):
+    import torch
+    if o.dtype == torch.bfloat16:
+        return COWA_DTYPE_BF16
+    if o.dtype == torch.float32:
+        return COWA_DTYPE_F32
+    raise TypeError("o must be bfloat16 or float32")
+
+
+def cowa_fwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
+             q, k, v, o, lse, softmax_scale: float, stream=None):
+    """Prefill forward.  q/o [B,N,H_q,d], k/v [B,N,H_kv,d] (bf16), lse [B,H_q,N] fp32."""
+    import torch
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v must be bfloat16 GPU tensors")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
+        raise ValueError("k and v must be [B, N, H_kv, d] matching q")
+    if tuple(o.shape) != (B, N, Hq, d) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o must be [B, N, H_q, d] and lse [B, H_q, N]")
+    strides = (ctypes.c_int64 * 12)(*(_strides(q, 3) + _strides(k, 3) + _strides(v, 3)
+                                      + _strides(o, 3)))
+    st = load().cowa_fwd(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
+                         nnz, block_m, block_n, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         o.data_ptr(), _o_dtype(o), lse.data_ptr(), B, N, Hq, Hkv, d,
+                         strides, float(softmax_scale), _stream_ptr(stream))
+    _check(st, "cowa_fwd")
+
+
+def cowa_decode_workspace_size(p: cowa_pattern, B: int, H_q: int, H_kv_local: int, d: int,
+                               n_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().cowa_decode_workspace_size(ctypes.byref(p), B, H_q, H_kv_local, d, n_max,
+                                             ctypes.byref(n)), "cowa_decode_workspace_size")
+    return n.value
+
+
+def cowa_decode(p: cowa_pattern, q, k_cache, v_cache, cache_seqlens, o, lse,
+                softmax_scale: float, workspace, stream=None):
+    """Decode.  q/o [B,H_q,d]; caches [B,n_max,H_kv,d] bf16; seqlens int32[B]; lse [B,H_q]."""
+    import torch
+    for t in (q, k_cache, v_cache):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q and caches must be bfloat16 GPU tensors")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be an int32 GPU tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    B, Hq, d = q.shape
+    _, n_max, Hkv, _ = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("caches must be [B, n_max, H_kv, d]")
+    if tuple(o.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("o must be [B, H_q, d] and lse [B, H_q]")
+    strides = (ctypes.c_int64 * 10)(*(_strides(q, 2) + _strides(k_cache, 3)
+                                      + _strides(v_cache, 3) + _strides(o, 2)))
+    st = load().cowa_decode(ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(),
+                            v_cache.data_ptr(), cache_seqlens.data_ptr(), o.data_ptr(),
+                            _o_dtype(o), lse.data_ptr(), B, Hq, Hkv, d, n_max, strides,
+                            float(softmax_scale), workspace.data_ptr(), workspace.numel()
+                            * workspace.element_size(), _stream_ptr(stream))
+    _check(st, "cowa_decode")

@@ -1,0 +1,224 @@
+// libcowa C ABI: argument validation and dispatch to the gfx950 kernels.
+// Every check runs on the host before anything is launched.
+#include <math.h>
+
+#include "cowa_internal.h"
+
+namespace cowa {
+
+cowa_status validate_pattern(const cowa_pattern* p, int32_t h_kv_local) {
+  if (!p) return COWA_ERR_INVALID_ARG;
+  if (p->mode != COWA_MODE_COWA && p->mode != COWA_MODE_CAUSAL) return COWA_ERR_INVALID_ARG;
+  if (p->n_ctx < 1 || p->sink < 0 || p->window < 1 || p->h_kv_global < 1 ||
+      p->kv_head_offset < 0)
+    return COWA_ERR_INVALID_ARG;
+  if (h_kv_local < 1 || (int64_t)p->kv_head_offset + h_kv_local > p->h_kv_global)
+    return COWA_ERR_INVALID_ARG;
+  return COWA_OK;
+}
+
+int32_t resolve_band(const cowa_pattern* p) {
+  return p->band > 0 ? p->band : derive_band(p->n_ctx, p->window, p->h_kv_global);
+}
+
+DecodeGeometry decode_geometry(const cowa_pattern* p, int32_t B, int32_t H_q, int32_t H_kv_local,
+                               int32_t d, int32_t n_max) {
+  DecodeGeometry g;
+  const int32_t L = resolve_band(p);
+  const int32_t max_vis = max_row_count(p->sink, p->window, L, p->mode == COWA_MODE_CAUSAL, n_max);
+  // aim for ~2048 workgroups (8 per compute unit) over all (b, head, split)
+  const int64_t pairs = (int64_t)B * H_kv_local;
+  int64_t want_splits = (2048 + pairs - 1) / pairs;
+  if (want_splits < 1) want_splits = 1;
+  int64_t chunk = (max_vis + want_splits - 1) / want_splits;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  if (chunk > kDecodeChunkMax) chunk = kDecodeChunkMax;
+  g.chunk = (int32_t)chunk;
+  g.n_splits = (int32_t)((max_vis + chunk - 1) / chunk);
+  g.opart_bytes = (size_t)g.n_splits * B * H_q * d * sizeof(float);
+  g.lse_offset = (g.opart_bytes + 255) / 256 * 256;
+  g.total_bytes = g.lse_offset + (size_t)g.n_splits * B * H_q * sizeof(float);
+  return g;
+}
+
+}  // namespace cowa
+
+using namespace cowa;
+
+extern "C" const char* cowa_status_str(cowa_status s) {
+  switch (s) {
+    case COWA_OK: return "ok";
+    case COWA_ERR_INVALID_ARG: return "invalid argument";
+    case COWA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case COWA_ERR_WORKSPACE: return "workspace missing or too small";
+    case COWA_ERR_PLAN_MISMATCH: return "plan does not match pattern, shape or tile";
+    case COWA_ERR_HIP: return "HIP launch failed";
+    case COWA_ERR_CAPACITY: return "plan buffers too small";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t cowa_band_length(const cowa_pattern* p) {
+  if (!p || validate_pattern(p, 1) != COWA_OK) return -1;
+  return resolve_band(p);
+}
+
+extern "C" cowa_status cowa_fwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n) {
+  if (!block_m || !block_n) return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  *block_m = kFwdBlockM;
+  *block_n = kFwdBlockN;
+  return COWA_OK;
+}
+
+// Plan sizes of recently seen shapes, per thread, so that checking a plan
+// against its pattern does not rebuild it on every call.
+static cowa_status plan_size_memo(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                                  int32_t bm, int32_t bn, int64_t* nnz) {
+  struct Entry {
+    cowa_pattern p;
+    int32_t n, h, bm, bn;
+    int64_t nnz;
+    bool used;
+  };
+  thread_local Entry memo[8] = {};
+  thread_local int next = 0;
+  for (auto& e : memo) {
+    if (e.used && e.n == n && e.h == h_kv_local && e.bm == bm && e.bn == bn &&
+        e.p.n_ctx == p->n_ctx && e.p.sink == p->sink && e.p.window == p->window &&
+        e.p.band == p->band && e.p.h_kv_global == p->h_kv_global &&
+        e.p.kv_head_offset == p->kv_head_offset && e.p.mode == p->mode) {
+      *nnz = e.nnz;
+      return COWA_OK;
+    }
+  }
+  cowa_status st = plan_impl(p, n, h_kv_local, bm, bn, nullptr, nullptr, nullptr, 0, nnz);
+  if (st != COWA_OK) return st;
+  memo[next] = Entry{*p, n, h_kv_local, bm, bn, *nnz, true};
+  next = (next + 1) & 7;
+  return COWA_OK;
+}
+
+static bool strides_ok(const int64_t* s, int n) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0) return false;
+  return true;
+}
+
+extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
+                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                                int32_t block_m, int32_t block_n, const void* q, const void* k,
+                                const void* v, void* o, int32_t o_dtype, float* lse, int32_t B,
+                                int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
+                                const int64_t strides[12], float softmax_scale, void* stream) {
+  cowa_status st = validate_pattern(p, H_kv_local);
+  if (st != COWA_OK) return st;
+  if (!d_row_ptr || !d_col || !d_flags || !q || !k || !v || !o || !lse || !strides)
+    return COWA_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || H_q < 1 || H_q % H_kv_local != 0) return COWA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
+  if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 12)) return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  if (block_m != kFwdBlockM || block_n != kFwdBlockN) return COWA_ERR_UNSUPPORTED;
+  const int64_t nqt = (N + block_m - 1) / block_m;
+  if ((int64_t)B * nqt * H_q > 0x7fffffffLL) return COWA_ERR_UNSUPPORTED;
+  int64_t want = 0;
+  st = plan_size_memo(p, N, H_kv_local, block_m, block_n, &want);
+  if (st != COWA_OK) return st;
+  if (want != nnz) return COWA_ERR_PLAN_MISMATCH;
+
+  FwdParams fp;
+  fp.row_ptr = d_row_ptr;
+  fp.col = d_col;
+  fp.flags = d_flags;
+  fp.q = static_cast<const uint16_t*>(q);
+  fp.k = static_cast<const uint16_t*>(k);
+  fp.v = static_cast<const uint16_t*>(v);
+  fp.o = o;
+  fp.lse = lse;
+  fp.qs_b = strides[0]; fp.qs_t = strides[1]; fp.qs_h = strides[2];
+  fp.ks_b = strides[3]; fp.ks_t = strides[4]; fp.ks_h = strides[5];
+  fp.vs_b = strides[6]; fp.vs_t = strides[7]; fp.vs_h = strides[8];
+  fp.os_b = strides[9]; fp.os_t = strides[10]; fp.os_h = strides[11];
+  fp.B = B;
+  fp.N = N;
+  fp.Hq = H_q;
+  fp.Hkv = H_kv_local;
+  fp.G = H_q / H_kv_local;
+  fp.nqt = (int32_t)nqt;
+  fp.sink = p->sink;
+  fp.window = p->window;
+  fp.band = resolve_band(p);
+  fp.kv_head_offset = p->kv_head_offset;
+  fp.causal = p->mode == COWA_MODE_CAUSAL;
+  fp.scale = softmax_scale;
+  fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launch_fwd(fp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,
+                                                  int32_t H_kv_local, int32_t d, int32_t n_max,
+                                                  size_t* bytes) {
+  cowa_status st = validate_pattern(p, H_kv_local);
+  if (st != COWA_OK) return st;
+  if (!bytes || B < 1 || H_q < 1 || H_q % H_kv_local != 0 || n_max < 1)
+    return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  *bytes = decode_geometry(p, B, H_q, H_kv_local, d, n_max).total_bytes;
+  return COWA_OK;
+}
+
+extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* cache_seqlens, void* o,
+                                   int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
+                                   int32_t H_kv_local, int32_t d, int32_t n_max,
+                                   const int64_t strides[10], float softmax_scale,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  cowa_status st = validate_pattern(p, H_kv_local);
+  if (st != COWA_OK) return st;
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse || !strides)
+    return COWA_ERR_INVALID_ARG;
+  if (B < 1 || H_q < 1 || n_max < 1 || H_q % H_kv_local != 0) return COWA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
+  if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 10)) return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  const int32_t G = H_q / H_kv_local;
+  if (G > kDecodeMaxGroup) return COWA_ERR_UNSUPPORTED;
+  const DecodeGeometry geo = decode_geometry(p, B, H_q, H_kv_local, d, n_max);
+  if ((int64_t)geo.n_splits > 0x7fffffffLL || B > 65535 || H_kv_local > 65535)
+    return COWA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < geo.total_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return COWA_ERR_WORKSPACE;
+
+  DecodeParams dp;
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.k = static_cast<const uint16_t*>(k_cache);
+  dp.v = static_cast<const uint16_t*>(v_cache);
+  dp.seqlens = cache_seqlens;
+  dp.o = o;
+  dp.lse = lse;
+  dp.opart = static_cast<float*>(workspace);
+  dp.lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.lse_offset);
+  dp.qs_b = strides[0]; dp.qs_h = strides[1];
+  dp.ks_b = strides[2]; dp.ks_t = strides[3]; dp.ks_h = strides[4];
+  dp.vs_b = strides[5]; dp.vs_t = strides[6]; dp.vs_h = strides[7];
+  dp.os_b = strides[8]; dp.os_h = strides[9];
+  dp.B = B;
+  dp.Hq = H_q;
+  dp.Hkv = H_kv_local;
+  dp.G = G;
+  dp.n_max = n_max;
+  dp.sink = p->sink;
+  dp.window = p->window;
+  dp.band = resolve_band(p);
+  dp.kv_head_offset = p->kv_head_offset;
+  dp.causal = p->mode == COWA_MODE_CAUSAL;
+  dp.chunk = geo.chunk;
+  dp.n_splits = geo.n_splits;
+  dp.scale = softmax_scale;
+  dp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launch_decode(dp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}

@@ -1,0 +1,111 @@
+// Position arithmetic of the CoWA pattern, shared by the host plan and the
+// device kernels.
+//
+// "Splitting long-range windows across KV heads beats duplicating them at
+// lower cost" (mechanism paragraph) and "CoWindow Attention: Full Causal
+// Coverage Is a Collective Property" (Abstract): every KV head sees a shared
+// prefix-sink window and a shared near-diagonal window; the remaining causal
+// history is cut into non-overlapping long-range bands, one per global KV
+// head.  The band partition used here (the pages give no formula):
+//   L = ceil((n_ctx - W) / H_kv_global) if n_ctx > W else 0,
+//   head g sees distances t - j in [W + g*L, W + (g+1)*L).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define COWA_HD __host__ __device__ __forceinline__
+#else
+#define COWA_HD inline
+#endif
+
+namespace cowa {
+
+COWA_HD int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+COWA_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+
+COWA_HD int32_t derive_band(int32_t n_ctx, int32_t window, int32_t h_kv_global) {
+  if (n_ctx <= window) return 0;
+  int64_t rest = (int64_t)n_ctx - window;
+  return (int32_t)((rest + h_kv_global - 1) / h_kv_global);
+}
+
+// Parameters of one global KV head, with the band bounds expressed as
+// distances.  Band distances [band_lo, band_hi); band_hi == band_lo when L == 0.
+struct HeadPattern {
+  int32_t sink;
+  int32_t window;
+  int32_t band_lo;
+  int32_t band_hi;
+  int32_t causal;  // 1: dense causal mode
+};
+
+COWA_HD HeadPattern head_pattern(int32_t sink, int32_t window, int32_t band, int32_t g,
+                                 int32_t causal) {
+  HeadPattern h;
+  h.sink = sink;
+  h.window = window;
+  // distances can exceed int32 only for absurd n_ctx; clamp in 64-bit
+  int64_t lo = (int64_t)window + (int64_t)g * band;
+  int64_t hi = lo + band;
+  h.band_lo = lo > 0x3fffffff ? 0x3fffffff : (int32_t)lo;
+  h.band_hi = hi > 0x3fffffff ? 0x3fffffff : (int32_t)hi;
+  h.causal = causal;
+  return h;
+}
+
+// Element predicate vis_g(t, j).
+COWA_HD bool visible(const HeadPattern& h, int32_t t, int32_t j) {
+  int32_t dist = t - j;
+  if (j < 0 || dist < 0) return false;
+  if (h.causal) return true;
+  return j < h.sink || dist < h.window || (dist >= h.band_lo && dist < h.band_hi);
+}
+
+// Visible keys of query row t as three disjoint half-open ranges in
+// ascending key order: sink [0, s_end), band [b_lo, b_hi), local [l_lo, t+1).
+// Empty ranges have lo == hi.  In causal mode the whole prefix is returned as
+// the "local" range.
+struct RowRanges {
+  int32_t lo[3];
+  int32_t hi[3];
+};
+
+COWA_HD RowRanges row_ranges(const HeadPattern& h, int32_t t) {
+  RowRanges r;
+  if (h.causal) {
+    r.lo[0] = r.hi[0] = 0;
+    r.lo[1] = r.hi[1] = 0;
+    r.lo[2] = 0;
+    r.hi[2] = t + 1;
+    return r;
+  }
+  int32_t s_end = imin(h.sink, t + 1);
+  int32_t l_lo = imax(imax(t - h.window + 1, 0), s_end);
+  // band keys: t - band_hi < j <= t - band_lo, kept above the sink and below
+  // the local window (distances >= W never reach the local window)
+  int32_t b_lo = imax(t - h.band_hi + 1, s_end);
+  int32_t b_hi = imin(t - h.band_lo + 1, l_lo);
+  if (b_hi < b_lo) b_hi = b_lo;
+  r.lo[0] = 0;
+  r.hi[0] = s_end;
+  r.lo[1] = b_lo;
+  r.hi[1] = b_hi;
+  r.lo[2] = l_lo;
+  r.hi[2] = t + 1;
+  return r;
+}
+
+COWA_HD int32_t row_count(const RowRanges& r) {
+  return (r.hi[0] - r.lo[0]) + (r.hi[1] - r.lo[1]) + (r.hi[2] - r.lo[2]);
+}
+
+// Largest number of keys any row can see: bounds the decode split count.
+COWA_HD int32_t max_row_count(int32_t sink, int32_t window, int32_t band, int32_t causal,
+                              int32_t n_keys) {
+  if (causal) return n_keys;
+  int64_t m = (int64_t)sink + window + band;
+  return m < n_keys ? (int32_t)m : n_keys;
+}
+
+}  // namespace cowa

@@ -1,0 +1,367 @@
+// CoWA single-token decode for gfx950: split-KV, HBM-streaming, two kernels.
+//
+// The decode query of sequence b sits at t = len_b - 1 and sees, per KV head
+// g, the same visible set as prefill row t: shared sink, shared local window
+// and band g ("CoWindow Attention: Full Causal Coverage Is a Collective
+// Property", Abstract: one pattern for training and inference).  Those keys
+// form at most three disjoint ranges; the split kernel walks their
+// concatenation in chunks, so only visible K/V rows are ever read.
+//
+// Split kernel, one workgroup per (chunk, KV head, sequence), 4 wavefronts:
+//   phase A  4 lanes per key (d/4 dims each) dot the key with all G query
+//            heads of the KV head (packed bf16 dot products, quad reduction)
+//            and store scaled scores in LDS;
+//   phase B  block max per head, then p = exp2(s - max) in LDS and the row
+//            sums;
+//   phase C  d/8 lanes per key (8 dims each) accumulate p * v for the G heads
+//            in fp32, reduced across lanes and wavefronts at the end.
+// The chunk's normalised output and log-sum-exp go to the workspace.
+// Combine kernel, one wavefront per (sequence, query head): merges the chunks
+// by their log-sum-exp.
+#include <hip/hip_runtime.h>
+
+#include "cowa_internal.h"
+
+namespace cowa {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NTHREADS = 256;
+constexpr int NWAVES = 4;
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float LN2 = 0.69314718055994531f;
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+struct Segs {
+  int lo0, n0, lo1, n1, lo2, n2;
+  __device__ int key(int v) const {
+    if (v < n0) return lo0 + v;
+    v -= n0;
+    if (v < n1) return lo1 + v;
+    return lo2 + v - n1;
+  }
+  __device__ int total() const { return n0 + n1 + n2; }
+};
+
+__device__ __forceinline__ Segs decode_segs(const DecodeParams& p, int b, int h, int* t_out) {
+  int len = p.seqlens[b];
+  len = len < 1 ? 1 : (len > p.n_max ? p.n_max : len);
+  const int t = len - 1;
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+  const RowRanges rr = row_ranges(hp, t);
+  Segs s;
+  s.lo0 = rr.lo[0];
+  s.n0 = rr.hi[0] - rr.lo[0];
+  s.lo1 = rr.lo[1];
+  s.n1 = rr.hi[1] - rr.lo[1];
+  s.lo2 = rr.lo[2];
+  s.n2 = rr.hi[2] - rr.lo[2];
+  *t_out = t;
+  return s;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
+  constexpr int GP = (G + 3) / 4 * 4;   // padded head count of an LDS score row
+  constexpr int DPL = D / 4;            // phase A: dims per lane
+  constexpr int NVA = DPL / 8;          // phase A: 16-byte loads per lane
+  constexpr int LPV = D / 8;            // phase C: lanes per key
+  constexpr int KPW = 64 / LPV;         // phase C: keys per wavefront step
+  constexpr int UA = 2;                 // phase A unroll (keys per quad in flight)
+  constexpr int UC = 4;                 // phase C unroll
+
+  __shared__ __attribute__((aligned(16))) float sc[kDecodeChunkMax * GP];
+  __shared__ float red[NWAVES][GP];
+  __shared__ float stat_m[GP];
+  __shared__ float stat_l[GP];
+  __shared__ __attribute__((aligned(16))) float accs[NWAVES][G * D];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  int t;
+  const Segs sg = decode_segs(p, b, h, &t);
+  const int nvis = sg.total();
+  const int v0 = split * p.chunk;
+  if (v0 >= nvis) return;
+  const int cnt = (nvis - v0) < p.chunk ? (nvis - v0) : p.chunk;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
+  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+
+  // ---- phase A: scores ----
+  {
+    const int quad = lane >> 2;
+    const int part = lane & 3;
+    u32x4 qr[G][NVA];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const uint16_t* qp = p.q + (int64_t)b * p.qs_b + (int64_t)(h * G + hh) * p.qs_h + part * DPL;
+#pragma unroll
+      for (int i = 0; i < NVA; ++i) qr[hh][i] = ldg16(qp + 8 * i);
+    }
+    float mx[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) mx[hh] = NEG_INF;
+
+    for (int base = wave * 16 + quad; base < cnt; base += 64 * UA) {
+      u32x4 kr[UA][NVA];
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int kk = base + 64 * u;
+        if (kk < cnt) {
+          const int key = sg.key(v0 + kk);
+          const uint16_t* kp = kbase + (int64_t)key * p.ks_t + part * DPL;
+#pragma unroll
+          for (int i = 0; i < NVA; ++i) kr[u][i] = ldg16(kp + 8 * i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int kk = base + 64 * u;
+        if (kk < cnt) {
+          float sv[G];
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < NVA; ++i)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) a = dot2(kr[u][i][w], qr[hh][i][w], a);
+            a += __shfl_xor(a, 1);
+            a += __shfl_xor(a, 2);
+            sv[hh] = a * p.scale_log2;
+            mx[hh] = fmaxf(mx[hh], sv[hh]);
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh)
+            if ((hh & 3) == part) sc[kk * GP + hh] = sv[hh];
+        }
+      }
+    }
+    // wave max over the 16 quads, then across waves
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float m = mx[hh];
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 8));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (lane == 0) red[wave][hh] = m;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) m = fmaxf(m, red[w][tid]);
+    stat_m[tid] = m;
+  }
+  __syncthreads();
+
+  // ---- phase B: probabilities and row sums ----
+  {
+    float ls[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) ls[hh] = 0.f;
+    for (int kk = tid; kk < cnt; kk += NTHREADS) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float e = __builtin_amdgcn_exp2f(sc[kk * GP + hh] - stat_m[hh]);
+        sc[kk * GP + hh] = e;
+        ls[hh] += e;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float s = ls[hh];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 8);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (lane == 0) red[wave][hh] = s;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) s += red[w][tid];
+    stat_l[tid] = s;
+  }
+
+  // ---- phase C: P.V ----
+  {
+    const int ksl = lane / LPV;   // key slot within the wavefront step
+    const int dp = lane % LPV;    // 8-dim part
+    float acc[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+
+    for (int base = wave * KPW + ksl; base < cnt; base += NWAVES * KPW * UC) {
+      u32x4 vr[UC];
+#pragma unroll
+      for (int u = 0; u < UC; ++u) {
+        const int kk = base + NWAVES * KPW * u;
+        if (kk < cnt) {
+          const int key = sg.key(v0 + kk);
+          vr[u] = ldg16(vbase + (int64_t)key * p.vs_t + dp * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UC; ++u) {
+        const int kk = base + NWAVES * KPW * u;
+        if (kk < cnt) {
+          float vf[8];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            vf[2 * w] = bf_lo(vr[u][w]);
+            vf[2 * w + 1] = bf_hi(vr[u][w]);
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            const float pr = sc[kk * GP + hh];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(pr, vf[e], acc[hh][e]);
+          }
+        }
+      }
+    }
+    // reduce over key slots (lanes dp, dp+LPV, ...)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = acc[hh][e];
+#pragma unroll
+        for (int off = LPV; off < 64; off <<= 1) a += __shfl_xor(a, off);
+        acc[hh][e] = a;
+      }
+    if (ksl == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        *reinterpret_cast<f32x4*>(&accs[wave][hh * D + dp * 8]) =
+            f32x4{acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]};
+        *reinterpret_cast<f32x4*>(&accs[wave][hh * D + dp * 8 + 4]) =
+            f32x4{acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]};
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- write this chunk's normalised output and log-sum-exp ----
+  const int64_t pidx = ((int64_t)split * p.B + b) * p.Hq + (int64_t)h * G;
+  for (int idx = tid; idx < G * D; idx += NTHREADS) {
+    const int hh = idx / D;
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) a += accs[w][idx];
+    p.opart[(pidx + hh) * D + (idx - hh * D)] = a / stat_l[hh];
+  }
+  if (tid < G) p.lsepart[pidx + tid] = (stat_m[tid] + __log2f(stat_l[tid])) * LN2;
+}
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(64) void cowa_decode_combine(DecodeParams p) {
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int h = hq / p.G;
+  int t;
+  const Segs sg = decode_segs(p, b, h, &t);
+  const int ns = (sg.total() + p.chunk - 1) / p.chunk;
+  const int lane = threadIdx.x;
+  const int64_t stride_s = (int64_t)p.B * p.Hq;
+  const int64_t base = (int64_t)b * p.Hq + hq;
+
+  float m = NEG_INF;
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, p.lsepart[s * stride_s + base]);
+  constexpr int DPT = D / 64;  // dims per lane
+  float o[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) o[i] = 0.f;
+  float wsum = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __expf(p.lsepart[s * stride_s + base] - m);
+    wsum += w;
+    const float* op = p.opart + (s * stride_s + base) * D;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(w, op[lane * DPT + i], o[i]);
+  }
+  const float inv = 1.f / wsum;
+  char* obase = reinterpret_cast<char*>(p.o);
+  const int64_t oidx = (int64_t)b * p.os_b + (int64_t)hq * p.os_h + lane * DPT;
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    if (OF32)
+      reinterpret_cast<float*>(obase)[oidx + i] = o[i] * inv;
+    else
+      reinterpret_cast<__bf16*>(obase)[oidx + i] = (__bf16)(o[i] * inv);
+  }
+  if (lane == 0) p.lse[base] = m + __logf(wsum);
+}
+
+template <int D, int G>
+void launch_split(const DecodeParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.n_splits, (unsigned)p.Hkv, (unsigned)p.B);
+  hipLaunchKernelGGL((cowa_decode_split<D, G>), grid, dim3(NTHREADS), 0, s, p);
+}
+
+template <int D>
+int dispatch_group(const DecodeParams& p, hipStream_t s) {
+  switch (p.G) {
+    case 1: launch_split<D, 1>(p, s); break;
+    case 2: launch_split<D, 2>(p, s); break;
+    case 3: launch_split<D, 3>(p, s); break;
+    case 4: launch_split<D, 4>(p, s); break;
+    case 5: launch_split<D, 5>(p, s); break;
+    case 6: launch_split<D, 6>(p, s); break;
+    case 7: launch_split<D, 7>(p, s); break;
+    case 8: launch_split<D, 8>(p, s); break;
+    default: return 1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int bad = d == 128 ? dispatch_group<128>(p, s) : dispatch_group<64>(p, s);
+  if (bad) return (int)hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  const dim3 grid((unsigned)p.Hq, (unsigned)p.B);
+  if (d == 128) {
+    if (o_f32) hipLaunchKernelGGL((cowa_decode_combine<128, true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((cowa_decode_combine<128, false>), grid, dim3(64), 0, s, p);
+  } else {
+    if (o_f32) hipLaunchKernelGGL((cowa_decode_combine<64, true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((cowa_decode_combine<64, false>), grid, dim3(64), 0, s, p);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace cowa

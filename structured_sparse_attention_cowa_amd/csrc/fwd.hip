@@ -1,0 +1,297 @@
+// CoWA prefill forward for gfx950 (CDNA4): bf16 MFMA, LDS-staged K/V tiles,
+// fp32 online softmax, driven by the visible-tile lists of cowa_plan.
+//
+// What is computed ("CoWindow Attention: Full Causal Coverage Is a
+// Collective Property", Abstract; "Splitting long-range windows across KV
+// heads beats duplicating them at lower cost", mechanism paragraph and the
+// paragraph on what CoWA does not claim): for every query head, a softmax over
+// that head's own visible keys (shared sink, shared local window, the band of
+// its global KV head).  Only the key tiles the plan lists are loaded; only
+// tiles the plan marks partial are masked.
+//
+// Workgroup = 4 wavefronts = 128 query rows of one (batch, query head).
+// Each wavefront owns 32 query rows and works in the transposed frame:
+//   S^T (32 keys x 32 queries) = K (32 x d) . Q^T (d x 32)     [MFMA 32x32x16]
+//   O^T (d x 32 queries)      += V^T (d x 64) . P^T (64 x 32)   [MFMA 32x32x16]
+// so every lane owns one query column: its softmax statistics are per-lane
+// scalars, the row max needs one exchange with the lane 32 away, and the
+// accumulator rescale is a per-lane scalar multiply.  The P^T operand of the
+// second product is the first product's accumulator, converted to bf16 in
+// place: the key order inside each 16-key step follows the accumulator
+// layout, and V^T is stored in LDS with the same key permutation.
+#include <hip/hip_runtime.h>
+
+#include "cowa_internal.h"
+
+namespace cowa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup
+constexpr int BN = kFwdBlockN;  // 64 keys per tile
+constexpr int NTHREADS = 256;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// position of key kk (0..63) of a tile inside an LDS V^T row: within every
+// 16-key group the middle two groups of four swap places, matching the key
+// order of the S^T accumulator registers (lane half 0 holds keys 0-3, 8-11;
+// half 1 holds 4-7, 12-15).
+__device__ __forceinline__ int vt_pos(int kk) {
+  const int g4 = (kk >> 2) & 3;
+  const int sw = (g4 == 1) ? 2 : (g4 == 2 ? 1 : g4);
+  return (kk & ~15) | (sw << 2) | (kk & 3);
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  bf16x2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, r);
+}
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(NTHREADS) void cowa_fwd_kernel(FwdParams p) {
+  constexpr int KSTR = D + 8;       // LDS K row stride (bf16 elements)
+  constexpr int VSTR = BN + 8;      // LDS V^T row stride
+  constexpr int KBUF = BN * KSTR;
+  constexpr int VBUF = D * VSTR;
+  constexpr int KCH = BN * D / 8 / NTHREADS;  // 16-byte K chunks per thread
+  constexpr int VCOMBOS = (BN / 4) * (D / 8); // (4 keys x 8 dims) blocks per V tile
+  constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
+  constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KBUF + VBUF)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  // heavy-first order: later query tiles see more keys
+  const int per_b = p.nqt * p.Hq;
+  const int wg = blockIdx.x;
+  const int b = wg / per_b;
+  const int rem = wg - b * per_b;
+  const int qi = p.nqt - 1 - rem / p.Hq;
+  const int hq = rem - (rem / p.Hq) * p.Hq;
+  const int h = hq / p.G;
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+
+  const int q_row = qi * BM + wave * 32 + l32;
+  const int q_row_c = q_row < p.N ? q_row : p.N - 1;
+
+  bf16x8 qf[NK];
+  {
+    const uint16_t* qp = p.q + (int64_t)b * p.qs_b + (int64_t)q_row_c * p.qs_t + (int64_t)hq * p.qs_h;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks + 8 * hl));
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
+  float m_run = NEG_INF;
+  float l_run = 0.f;
+
+  const int row = h * p.nqt + qi;
+  const int e0 = p.row_ptr[row];
+  const int e1 = p.row_ptr[row + 1];
+  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
+  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+
+  u32x4 kreg[KCH];
+  u32x4 vreg[4];
+  const int vkg = tid % (BN / 4);  // key group of 4 this thread transposes
+  const int vdc = tid / (BN / 4);  // 8-dim chunk
+  const bool vthread = tid < VCOMBOS;
+
+  auto gload = [&](int kj) {
+    const int key0 = kj * BN;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int r = c / (D / 8);
+      const int c8 = c - r * (D / 8);
+      const int key = key0 + r;
+      kreg[i] = key < p.N ? ldg16(kbase + (int64_t)key * p.ks_t + c8 * 8) : u32x4{0, 0, 0, 0};
+    }
+    if (vthread) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + vkg * 4 + r;
+        vreg[r] = key < p.N ? ldg16(vbase + (int64_t)key * p.vs_t + vdc * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto lstore = [&](int buf) {
+    uint16_t* Ks = smem + buf * KBUF;
+    uint16_t* Vt = smem + 2 * KBUF + buf * VBUF;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int r = c / (D / 8);
+      const int c8 = c - r * (D / 8);
+      *reinterpret_cast<u32x4*>(Ks + r * KSTR + c8 * 8) = kreg[i];
+    }
+    if (vthread) {
+      const int pos = vt_pos(vkg * 4);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // dims 2w and 2w+1 of keys 0..3
+        u32x2 ev, od;
+        ev.x = __byte_perm(vreg[0][w], vreg[1][w], 0x5410);
+        ev.y = __byte_perm(vreg[2][w], vreg[3][w], 0x5410);
+        od.x = __byte_perm(vreg[0][w], vreg[1][w], 0x7632);
+        od.y = __byte_perm(vreg[2][w], vreg[3][w], 0x7632);
+        const int dd = vdc * 8 + 2 * w;
+        *reinterpret_cast<u32x2*>(Vt + dd * VSTR + pos) = ev;
+        *reinterpret_cast<u32x2*>(Vt + (dd + 1) * VSTR + pos) = od;
+      }
+    }
+  };
+
+  if (e0 < e1) {
+    gload(p.col[e0]);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int e = e0; e < e1; ++e) {
+    const int buf = (e - e0) & 1;
+    const int kj = p.col[e];
+    const bool full = p.flags[e] != 0;
+    const bool has_next = e + 1 < e1;
+    if (has_next) gload(p.col[e + 1]);
+
+    const uint16_t* Ks = smem + buf * KBUF;
+    const uint16_t* Vt = smem + 2 * KBUF + buf * VBUF;
+
+    // S^T for keys [32*blk, 32*blk+32) of the tile
+    f32x16 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x16{};
+      const uint16_t* kr = Ks + (32 * blk + l32) * KSTR + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[blk], 0, 0, 0);
+      }
+    }
+
+    if (!full) {
+      const int key0 = kj * BN + 4 * hl;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * blk + 8 * (i >> 2) + (i & 3);
+          if (!visible(hp, q_row, key)) s[blk][i] = NEG_INF;
+        }
+    }
+
+    float mt = NEG_INF;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * p.scale_log2);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+
+    const float mb = m_use * p.scale_log2;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], p.scale_log2, -mb));
+        s[blk][i] = e2;
+        l_run += e2;
+      }
+
+    // O^T += V^T P^T, four 16-key steps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int blk = st >> 1;
+      const int o8 = (st & 1) * 8;
+      u32x4 pw;
+      pw.x = pack_bf16(s[blk][o8 + 0], s[blk][o8 + 1]);
+      pw.y = pack_bf16(s[blk][o8 + 2], s[blk][o8 + 3]);
+      pw.z = pack_bf16(s[blk][o8 + 4], s[blk][o8 + 5]);
+      pw.w = pack_bf16(s[blk][o8 + 6], s[blk][o8 + 7]);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, pw);
+      const uint16_t* vr = Vt + l32 * VSTR + 16 * st + 8 * hl;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + 32 * db * VSTR);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
+      }
+    }
+
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (q_row < p.N) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    char* obase = reinterpret_cast<char*>(p.o);
+    const int64_t oidx = (int64_t)b * p.os_b + (int64_t)q_row * p.os_t + (int64_t)hq * p.os_h;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int dd = 32 * db + 8 * gi + 4 * hl;
+        const float v0 = acc[db][4 * gi + 0] * inv, v1 = acc[db][4 * gi + 1] * inv;
+        const float v2 = acc[db][4 * gi + 2] * inv, v3 = acc[db][4 * gi + 3] * inv;
+        if (OF32) {
+          *reinterpret_cast<f32x4*>(obase + (oidx + dd) * 4) = f32x4{v0, v1, v2, v3};
+        } else {
+          *reinterpret_cast<u32x2*>(obase + (oidx + dd) * 2) =
+              u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        }
+      }
+    if (hl == 0) {
+      const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : NEG_INF;
+      p.lse[((int64_t)b * p.Hq + hq) * p.N + q_row] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_fwd(const FwdParams& p, int d, int o_f32, void* stream) {
+  const dim3 grid((unsigned)((int64_t)p.B * p.nqt * p.Hq));
+  const dim3 block(NTHREADS);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 128) {
+    if (o_f32)
+      hipLaunchKernelGGL((cowa_fwd_kernel<128, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((cowa_fwd_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    if (o_f32)
+      hipLaunchKernelGGL((cowa_fwd_kernel<64, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((cowa_fwd_kernel<64, false>), grid, block, 0, s, p);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace cowa

@@ -1,0 +1,206 @@
+"""CPU tests of the C ABI: exported symbols, the host plan (bit-exact against
+the oracle's independent tile enumeration) and host-side argument checks."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.cowa_oracle as O
+from structured_sparse_attention_cowa_amd import binding as C
+from structured_sparse_attention_cowa_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "cowa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|cowa_status|int32_t)\s+(cowa_\w+)\(",
+                                 txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTED)
+
+
+def test_status_strings(lib):
+    assert C.cowa_status_str(0) == "ok"
+    for s in range(1, 7):
+        assert C.cowa_status_str(s) != "unknown status"
+
+
+def pat(**kw):
+    base = dict(n_ctx=1024, sink=16, window=128, band=0, h_kv_global=4, kv_head_offset=0, mode=0)
+    base.update(kw)
+    return C.make_pattern(**base), O.Pattern(**base)
+
+
+def test_band_length_abi(lib):
+    for w in W.PREFILL_WORKLOADS:
+        cp, _ = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=w.h_kv_global)
+        assert C.cowa_band_length(cp) == w.stated_band
+    cp, _ = pat(n_ctx=W.D128K.n_ctx, sink=128, window=8192, h_kv_global=8)
+    assert C.cowa_band_length(cp) == 15360
+    cp, _ = pat(window=0)
+    assert C.cowa_band_length(cp) == -1
+    cp, _ = pat(band=77)
+    assert C.cowa_band_length(cp) == 77
+
+
+def compare_plan(cp, op, n, hkv, bm, bn, method="auto"):
+    rp, col, fl = C.cowa_plan(cp, n, hkv, bm, bn)
+    orp, ocol, ofl = O.tile_lists(n, hkv, op, bm, bn, method=method)
+    assert np.array_equal(rp, orp)
+    assert np.array_equal(col, ocol)
+    assert np.array_equal(fl, ofl)
+    assert C.cowa_plan_size(cp, n, hkv, bm, bn) == len(ocol)
+    return rp, col, fl
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("bm,bn", [(16, 16), (64, 64), (128, 64), (128, 128), (32, 48)])
+@pytest.mark.parametrize("n,S,Wd,H,off,hkv", [
+    (1024, 16, 128, 4, 0, 4),    # tiny workload, all heads
+    (1000, 16, 128, 4, 1, 3),    # ragged, offset
+    (17, 2, 4, 4, 0, 4),         # worked ragged case
+    (16, 2, 4, 4, 2, 2),
+    (333, 0, 1, 8, 5, 3),        # band only
+    (300, 7, 400, 4, 0, 4),      # window covers everything (L = 0)
+    (129, 129, 1, 2, 0, 2),      # sink covers everything
+    (1, 0, 1, 1, 0, 1),          # single token
+])
+def test_plan_bit_exact_small(lib, mode, bm, bn, n, S, Wd, H, off, hkv):
+    cp, op = pat(n_ctx=n, sink=S, window=Wd, h_kv_global=H, kv_head_offset=off, mode=mode)
+    compare_plan(cp, op, n, hkv, bm, bn, method="bruteforce" if n <= 1024 else "fast")
+
+
+@pytest.mark.parametrize("w", [W.P8K, W.P32K])
+def test_plan_bit_exact_workloads(lib, w):
+    cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=w.h_kv_global)
+    rp, col, fl = compare_plan(cp, op, w.N, w.H_kv, 128, 64, method="fast")
+    if w is W.P8K:
+        nqt = w.N // 128
+        nnz = np.diff(rp).reshape(w.H_kv, nqt).sum(1)
+        assert list(nnz[[0, 7]]) == [1856, 1184]
+
+
+def test_plan_8k_bruteforce_two_heads(lib):
+    w = W.P8K
+    for g in (0, 7):
+        cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8, kv_head_offset=g)
+        compare_plan(cp, op, w.N, 1, 128, 64, method="bruteforce")
+
+
+@pytest.mark.parametrize("g", range(8))
+def test_plan_bit_exact_128k_rank(lib, g):
+    w = W.P128K
+    cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8, kv_head_offset=g)
+    compare_plan(cp, op, w.N, 1, 128, 64, method="fast")
+
+
+def test_plan_128k_causal_size(lib):
+    cp, _ = pat(n_ctx=131072, sink=128, window=8192, h_kv_global=8, mode=1)
+    # causal, BM = 2 BN: query tile qi lists key tiles 0 .. 2qi+1
+    assert C.cowa_plan_size(cp, 131072, 1, 128, 64) == sum(2 * qi + 2 for qi in range(1024))
+
+
+def test_plan_capacity_and_invalid(lib):
+    cp, _ = pat()
+    nnz = C.cowa_plan_size(cp, 1024, 4, 128, 64)
+    rp = np.zeros(4 * 8 + 1, np.int32)
+    col = np.zeros(nnz, np.int32)
+    fl = np.zeros(nnz, np.uint8)
+    L = C.load()
+    st = L.cowa_plan(ctypes.byref(cp), 1024, 4, 128, 64, rp.ctypes.data, col.ctypes.data,
+                     fl.ctypes.data, nnz - 1)
+    assert st == C.COWA_ERR_CAPACITY
+    bad = [dict(window=0), dict(sink=-1), dict(h_kv_global=0), dict(kv_head_offset=2),
+           dict(mode=2), dict(n_ctx=0)]
+    for b in bad:
+        cpb, _ = pat(**b)
+        out = ctypes.c_int64()
+        assert L.cowa_plan_size(ctypes.byref(cpb), 1024, 4, 128, 64, ctypes.byref(out)) == \
+            C.COWA_ERR_INVALID_ARG, b
+    out = ctypes.c_int64()
+    assert L.cowa_plan_size(ctypes.byref(cp), 0, 4, 128, 64, ctypes.byref(out)) == \
+        C.COWA_ERR_INVALID_ARG
+    assert L.cowa_plan_size(None, 10, 1, 16, 16, ctypes.byref(out)) == C.COWA_ERR_INVALID_ARG
+
+
+def test_fwd_block_sizes(lib):
+    assert C.cowa_fwd_block_sizes(128) == (128, 64)
+    assert C.cowa_fwd_block_sizes(64) == (128, 64)
+    with pytest.raises(C.CowaError) as e:
+        C.cowa_fwd_block_sizes(96)
+    assert e.value.status == C.COWA_ERR_UNSUPPORTED
+
+
+def _fwd_raw(lib, cp, nnz=None, bm=128, bn=64, B=1, N=256, Hq=4, Hkv=2, d=128, scale=0.1,
+             o_dtype=0, null=None, strides=None):
+    """Calls cowa_fwd with fake (never dereferenced) device pointers: every
+    case here must be rejected on the host before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    ptrs = {k: fake for k in ("rp", "col", "fl", "q", "k", "v", "o", "lse")}
+    if null:
+        ptrs[null] = None
+    if nnz is None:
+        nnz = C.cowa_plan_size(cp, N, Hkv, 128, 64)
+    s = strides if strides is not None else [1] * 12
+    arr = (ctypes.c_int64 * 12)(*s)
+    return lib.cowa_fwd(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, bm, bn,
+                        ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], o_dtype, ptrs["lse"],
+                        B, N, Hq, Hkv, d, arr, scale, None)
+
+
+def test_fwd_host_validation(lib):
+    cp, _ = pat(n_ctx=256, h_kv_global=2)
+    E = C
+    assert _fwd_raw(lib, cp, nnz=3) == E.COWA_ERR_PLAN_MISMATCH
+    assert _fwd_raw(lib, cp, bm=64) == E.COWA_ERR_UNSUPPORTED
+    assert _fwd_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
+    assert _fwd_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, scale=0.0) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, scale=float("nan")) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, o_dtype=7) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, strides=[-1] + [1] * 11) == E.COWA_ERR_INVALID_ARG
+    for nm in ("rp", "col", "fl", "q", "k", "v", "o", "lse"):
+        assert _fwd_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
+    cp3, _ = pat(n_ctx=256, h_kv_global=2, kv_head_offset=1)
+    assert _fwd_raw(lib, cp3, nnz=1) == E.COWA_ERR_INVALID_ARG  # offset + H_kv_local > global
+    # a plan built for another window has another size
+    cp4, _ = pat(n_ctx=4096, h_kv_global=2)
+    cpw, _ = pat(n_ctx=4096, h_kv_global=2, window=64)
+    nnz_other = C.cowa_plan_size(cpw, 4096, 2, 128, 64)
+    assert nnz_other != C.cowa_plan_size(cp4, 4096, 2, 128, 64)
+    assert _fwd_raw(lib, cp4, nnz=nnz_other, N=4096) == E.COWA_ERR_PLAN_MISMATCH
+
+
+def test_decode_host_validation(lib):
+    cp, _ = pat(n_ctx=4096, sink=16, window=128, h_kv_global=4)
+    ws = C.cowa_decode_workspace_size(cp, 2, 8, 4, 128, 4096)
+    assert ws > 0
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(B=2, Hq=8, Hkv=4, d=128, nmax=4096, ws_ptr=ctypes.c_void_p(0x100000),
+             ws_bytes=ws, o_dtype=0, scale=0.1, p=cp):
+        arr = (ctypes.c_int64 * 10)(*([1] * 10))
+        return lib.cowa_decode(ctypes.byref(p), fake, fake, fake, fake, fake, o_dtype, fake, B,
+                               Hq, Hkv, d, nmax, arr, scale, ws_ptr, ws_bytes, None)
+
+    assert call(ws_bytes=ws - 1) == C.COWA_ERR_WORKSPACE
+    assert call(ws_ptr=None) == C.COWA_ERR_WORKSPACE
+    assert call(ws_ptr=ctypes.c_void_p(0x100010)) == C.COWA_ERR_WORKSPACE  # misaligned
+    assert call(d=80) == C.COWA_ERR_UNSUPPORTED
+    cp_g, _ = pat(n_ctx=4096, sink=16, window=128, h_kv_global=1)
+    ws16 = C.cowa_decode_workspace_size(cp_g, 2, 16, 1, 128, 4096)
+    assert call(Hq=16, Hkv=1, p=cp_g, ws_bytes=ws16) == C.COWA_ERR_UNSUPPORTED  # G = 16
+    assert call(Hq=6) == C.COWA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == C.COWA_ERR_INVALID_ARG
+    assert call(o_dtype=3) == C.COWA_ERR_INVALID_ARG
+    assert call(nmax=0) == C.COWA_ERR_INVALID_ARG
