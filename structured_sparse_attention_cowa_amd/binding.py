@@ -60,7 +60,12 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"libcowa.so not built at {LIB_PATH}; run "
                            "python -m structured_sparse_attention_cowa_amd.build")
+    # torch ships its own HIP runtime (same soname as the system one).  Loading
+    # torch first makes libcowa bind to that runtime, so device pointers and
+    # stream handles from torch are valid inside the library.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    _check_single_hip_runtime()
     P = ctypes.POINTER
     i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     pat = P(cowa_pattern)
@@ -84,6 +89,17 @@ def load():
                                 P(i64), f32, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
+
+
+def _check_single_hip_runtime():
+    """Two HIP runtimes in one process cannot share streams or allocations."""
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    if len(libs) > 1:
+        raise RuntimeError(f"two HIP runtimes are loaded in this process: {sorted(libs)}")
 
 
 def _check(st: int, where: str):

@@ -204,3 +204,11 @@ def test_decode_host_validation(lib):
     assert call(scale=-1.0) == C.COWA_ERR_INVALID_ARG
     assert call(o_dtype=3) == C.COWA_ERR_INVALID_ARG
     assert call(nmax=0) == C.COWA_ERR_INVALID_ARG
+
+
+def test_single_hip_runtime_after_load(lib):
+    """libcowa must share torch's HIP runtime: streams and allocations from
+    torch are only valid inside the runtime that created them."""
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
