@@ -74,12 +74,15 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
             torch.bfloat16).to(dev)
 
+    need_prefill = args.only in (None, "prefill")
+    need_decode = args.only in (None, "decode")
+
     # ---------------- prefill setup ----------------
     wp = W.P128K
-    x = W.prefill_inputs(wp)
-    q, k, v = to_dev(x.q_bits), to_dev(x.k_bits), to_dev(x.v_bits)
-    B, N, Hq, d = x.q_bits.shape
-    Hkv = x.k_bits.shape[2]
+    B, N, Hq, Hkv, d = wp.B, wp.N, wp.H_q, wp.H_kv, wp.d
+    if need_prefill:
+        x = W.prefill_inputs(wp)
+        q, k, v = to_dev(x.q_bits), to_dev(x.k_bits), to_dev(x.v_bits)
     o = torch.empty((B, N, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     bm, bn = C.cowa_fwd_block_sizes(d)
@@ -92,7 +95,7 @@ def main():
                 torch.from_numpy(fl).to(dev), len(col))
 
     t_plan0 = time.perf_counter()
-    plan0 = make_plan(0)
+    plan0 = make_plan(0) if need_prefill else None
     plan_ms = (time.perf_counter() - t_plan0) * 1e3
 
     def prefill(plan):
@@ -109,7 +112,8 @@ def main():
     wd = W.D128K
     lens = W.decode_lens(wd)
     qd = to_dev(W.decode_query(wd))
-    kc, vc = W.decode_cache_device(wd, lens, device=dev)
+    if need_decode:
+        kc, vc = W.decode_cache_device(wd, lens, device=dev)
     pd = C.make_pattern(wd.n_ctx, wd.sink, wd.window, 0, wd.h_kv_global, 0, 0)
     ws = torch.empty(C.cowa_decode_workspace_size(pd, wd.B, wd.H_q, wd.H_kv, wd.d, wd.n_max),
                      dtype=torch.uint8, device=dev)

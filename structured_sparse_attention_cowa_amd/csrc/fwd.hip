@@ -52,13 +52,41 @@ __device__ __forceinline__ int vt_pos(int kk) {
   return (kk & ~15) | (sw << 2) | (kk & 3);
 }
 
+// Lane l and lane l^32 hold the two halves of one query column; this returns
+// (value of lane l, value of lane l^32) in some order on every lane.
+__device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return a + b;
+}
+
+// The running maximum is only raised when a row's maximum grows by more than
+// 2^RESCALE_LOG2 in probability terms; until then the stale maximum is kept
+// and probabilities may reach 2^RESCALE_LOG2 (exact: the same reference
+// maximum is used for the sum and for the output).
+constexpr float RESCALE_LOG2 = 8.0f;
+
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   bf16x2 r = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(unsigned, r);
 }
 
 template <int D, bool OF32>
-__global__ __launch_bounds__(NTHREADS) void cowa_fwd_kernel(FwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
+                          amdgpu_waves_per_eu(2, 2))) void cowa_fwd_kernel(FwdParams p) {
   constexpr int KSTR = D + 8;       // LDS K row stride (bf16 elements)
   constexpr int VSTR = BN + 8;      // LDS V^T row stride
   constexpr int KBUF = BN * KSTR;
@@ -206,16 +234,21 @@ __global__ __launch_bounds__(NTHREADS) void cowa_fwd_kernel(FwdParams p) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * p.scale_log2);
-    m_run = m_new;
-    l_run *= alpha;
+    mt = pair_max(mt);
+    // raise the reference maximum only where it grew past the threshold
+    // (always on a row's first visible key: m_run = -inf gives +inf)
+    const bool grow = (mt - m_run) * p.scale_log2 > RESCALE_LOG2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha =
+          m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+      for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+    }
 
-    const float mb = m_use * p.scale_log2;
+    const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -248,7 +281,7 @@ __global__ __launch_bounds__(NTHREADS) void cowa_fwd_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (q_row < p.N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* obase = reinterpret_cast<char*>(p.o);
