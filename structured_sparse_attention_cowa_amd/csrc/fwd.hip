@@ -17,8 +17,15 @@
 // scalars, the row max needs one exchange with the lane 32 away, and the
 // accumulator rescale is a per-lane scalar multiply.  The P^T operand of the
 // second product is the first product's accumulator, converted to bf16 in
-// place: the key order inside each 16-key step follows the accumulator
-// layout, and V^T is stored in LDS with the same key permutation.
+// place; the key order inside each 16-key step follows the accumulator
+// layout (lane half 0 holds keys 0-3 and 8-11, half 1 keys 4-7 and 12-15).
+//
+// K and V tiles go from HBM straight into LDS (16 bytes per lane, no
+// register staging), row-major with the 16-byte chunks of each row XOR-
+// swizzled by the row index so that 16 consecutive rows read at one column
+// hit distinct banks.  K feeds the first product with 16-byte reads; V feeds
+// the second through the gfx950 transposing read (ds_read_b64_tr_b16), which
+// hands each lane four keys of one head dimension.
 #include <hip/hip_runtime.h>
 
 #include "cowa_internal.h"
@@ -40,16 +47,6 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-
-// position of key kk (0..63) of a tile inside an LDS V^T row: within every
-// 16-key group the middle two groups of four swap places, matching the key
-// order of the S^T accumulator registers (lane half 0 holds keys 0-3, 8-11;
-// half 1 holds 4-7, 12-15).
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int g4 = (kk >> 2) & 3;
-  const int sw = (g4 == 1) ? 2 : (g4 == 2 ? 1 : g4);
-  return (kk & ~15) | (sw << 2) | (kk & 3);
 }
 
 // Lane l and lane l^32 hold the two halves of one query column; this returns
@@ -84,19 +81,31 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One 16-byte chunk per lane from global memory straight into LDS; the
+// wavefront's 64 chunks land contiguously at lds_base (+16 bytes per lane).
+__device__ __forceinline__ void g2lds16(const uint16_t* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
 template <int D, bool OF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void cowa_fwd_kernel(FwdParams p) {
-  constexpr int KSTR = D + 8;       // LDS K row stride (bf16 elements)
-  constexpr int VSTR = BN + 8;      // LDS V^T row stride
-  constexpr int KBUF = BN * KSTR;
-  constexpr int VBUF = D * VSTR;
-  constexpr int KCH = BN * D / 8 / NTHREADS;  // 16-byte K chunks per thread
-  constexpr int VCOMBOS = (BN / 4) * (D / 8); // (4 keys x 8 dims) blocks per V tile
+  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int TILE = BN * D;                // bf16 elements per K or V tile
+  constexpr int LOADS = BN * CPR / 64 / 4;    // direct loads per wave per tile
   constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
   constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KBUF + VBUF)];
+  // [buffer][K tile, V tile]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,83 +146,71 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  const int vkg = tid % (BN / 4);  // key group of 4 this thread transposes
-  const int vdc = tid / (BN / 4);  // 8-dim chunk
-  const bool vthread = tid < VCOMBOS;
-
-  auto gload = [&](int kj) {
-    const int key0 = kj * BN;
+  // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
+  // holds row P / CPR, column chunk (P % CPR) ^ (row % CPR).
+  int ld_row[LOADS], ld_col[LOADS];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int r = c / (D / 8);
-      const int c8 = c - r * (D / 8);
-      const int key = key0 + r;
-      kreg[i] = key < p.N ? ldg16(kbase + (int64_t)key * p.ks_t + c8 * 8) : u32x4{0, 0, 0, 0};
-    }
-    if (vthread) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + vkg * 4 + r;
-        vreg[r] = key < p.N ? ldg16(vbase + (int64_t)key * p.vs_t + vdc * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
-  auto lstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * KBUF;
-    uint16_t* Vt = smem + 2 * KBUF + buf * VBUF;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int r = c / (D / 8);
-      const int c8 = c - r * (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + r * KSTR + c8 * 8) = kreg[i];
-    }
-    if (vthread) {
-      const int pos = vt_pos(vkg * 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 2w and 2w+1 of keys 0..3
-        u32x2 ev, od;
-        ev.x = __byte_perm(vreg[0][w], vreg[1][w], 0x5410);
-        ev.y = __byte_perm(vreg[2][w], vreg[3][w], 0x5410);
-        od.x = __byte_perm(vreg[0][w], vreg[1][w], 0x7632);
-        od.y = __byte_perm(vreg[2][w], vreg[3][w], 0x7632);
-        const int dd = vdc * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(Vt + dd * VSTR + pos) = ev;
-        *reinterpret_cast<u32x2*>(Vt + (dd + 1) * VSTR + pos) = od;
-      }
-    }
-  };
-
-  if (e0 < e1) {
-    gload(p.col[e0]);
-    lstore(0);
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (wave * LOADS + i) * 64 + lane;
+    ld_row[i] = P / CPR;
+    ld_col[i] = ((P % CPR) ^ (ld_row[i] % CPR)) * 8;
   }
+  // Keys past N are clamped to N - 1: such keys only occur in tiles the plan
+  // marks partial, where they are masked (their probability is exactly 0).
+  auto issue_loads = [&](int kj, int buf) {
+    const int key0 = kj * BN;
+    uint16_t* Ks = smem + buf * 2 * TILE;
+    uint16_t* Vs = Ks + TILE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int key = key0 + ld_row[i];
+      key = key < p.N ? key : p.N - 1;
+      const int off = (wave * LOADS + i) * 64 * 8;
+      g2lds16(kbase + (int64_t)key * p.ks_t + ld_col[i], Ks + off);
+      g2lds16(vbase + (int64_t)key * p.vs_t + ld_col[i], Vs + off);
+    }
+  };
+
+  // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl
+  int k_off[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) k_off[ks] = l32 * D + (((2 * ks + hl) ^ (l32 % CPR)) * 8);
+  // V transposed-read offsets (second product, A operand): for 16-key step st,
+  // d block db and half ri, lane reads key 16*st + 8*ri + 4*hl + (lane&15)/4 at
+  // dims 32*db + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
+  const int r16 = lane & 15;
+  const int gi = (lane >> 4) & 1;
+  int v_off[2][ND];
+#pragma unroll
+  for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int key = 8 * ri + 4 * hl + (r16 >> 2);
+      const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
+      v_off[ri][db] = key * D + (((d >> 3) ^ (key % CPR)) * 8) + (d & 7);
+    }
+
+  if (e0 < e1) issue_loads(p.col[e0], 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int e = e0; e < e1; ++e) {
     const int buf = (e - e0) & 1;
     const int kj = p.col[e];
     const bool full = p.flags[e] != 0;
-    const bool has_next = e + 1 < e1;
-    if (has_next) gload(p.col[e + 1]);
+    if (e + 1 < e1) issue_loads(p.col[e + 1], buf ^ 1);
 
-    const uint16_t* Ks = smem + buf * KBUF;
-    const uint16_t* Vt = smem + 2 * KBUF + buf * VBUF;
+    const uint16_t* Ks = smem + buf * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
 
     // S^T for keys [32*blk, 32*blk+32) of the tile
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
-      const uint16_t* kr = Ks + (32 * blk + l32) * KSTR + 8 * hl;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + blk * 32 * D + k_off[ks]);
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[blk], 0, 0, 0);
       }
     }
@@ -269,15 +266,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       pw.z = pack_bf16(s[blk][o8 + 4], s[blk][o8 + 5]);
       pw.w = pack_bf16(s[blk][o8 + 6], s[blk][o8 + 7]);
       const bf16x8 bv = __builtin_bit_cast(bf16x8, pw);
-      const uint16_t* vr = Vt + l32 * VSTR + 16 * st + 8 * hl;
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + 32 * db * VSTR);
+        const i16x4 lo = lds_read_tr(Vs + st * 16 * D + v_off[0][db]);
+        const i16x4 hi = lds_read_tr(Vs + st * 16 * D + v_off[1][db]);
+        const i16x4 a8[2] = {lo, hi};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
 
-    if (has_next) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -289,10 +288,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int dd = 32 * db + 8 * gi + 4 * hl;
-        const float v0 = acc[db][4 * gi + 0] * inv, v1 = acc[db][4 * gi + 1] * inv;
-        const float v2 = acc[db][4 * gi + 2] * inv, v3 = acc[db][4 * gi + 3] * inv;
+      for (int gi2 = 0; gi2 < 4; ++gi2) {
+        const int dd = 32 * db + 8 * gi2 + 4 * hl;
+        const float v0 = acc[db][4 * gi2 + 0] * inv, v1 = acc[db][4 * gi2 + 1] * inv;
+        const float v2 = acc[db][4 * gi2 + 2] * inv, v3 = acc[db][4 * gi2 + 3] * inv;
         if (OF32) {
           *reinterpret_cast<f32x4*>(obase + (oidx + dd) * 4) = f32x4{v0, v1, v2, v3};
         } else {
