@@ -122,6 +122,9 @@ extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   if (!strides_ok(strides, 12)) return COWA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (block_m != kFwdBlockM || block_n != kFwdBlockN) return COWA_ERR_UNSUPPORTED;
+  // per-lane offsets inside one K/V tile are 32-bit
+  if ((int64_t)block_n * strides[4] >= (1LL << 31) || (int64_t)block_n * strides[7] >= (1LL << 31))
+    return COWA_ERR_UNSUPPORTED;
   const int64_t nqt = (N + block_m - 1) / block_m;
   if ((int64_t)B * nqt * H_q > 0x7fffffffLL) return COWA_ERR_UNSUPPORTED;
   int64_t want = 0;

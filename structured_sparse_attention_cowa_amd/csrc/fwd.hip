@@ -104,12 +104,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
   constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
 
-  // [buffer][K tile, V tile]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+  // K tiles [2] then V tiles [2]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+  uint16_t* const Kbuf = smem;
+  uint16_t* const Vbuf = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
@@ -147,27 +149,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
 
   // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
-  // holds row P / CPR, column chunk (P % CPR) ^ (row % CPR).
-  int ld_row[LOADS], ld_col[LOADS];
+  // holds row P / CPR, column chunk (P % CPR) ^ (row % CPR).  Per-lane
+  // offsets inside a tile are fixed; the tile base is uniform.
+  int ld_row[LOADS], ld_col[LOADS], ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
     ld_col[i] = ((P % CPR) ^ (ld_row[i] % CPR)) * 8;
+    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_col[i];
+    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_col[i];
   }
-  // Keys past N are clamped to N - 1: such keys only occur in tiles the plan
-  // marks partial, where they are masked (their probability is exactly 0).
-  auto issue_loads = [&](int kj, int buf) {
+  // Loads of one K (or V) tile into LDS buffer dst.  Keys past N (ragged last
+  // tile) are clamped to N - 1: they only occur in tiles the plan marks
+  // partial, where they are masked (probability exactly 0).
+  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, int kj,
+                       uint16_t* dst) {
     const int key0 = kj * BN;
-    uint16_t* Ks = smem + buf * 2 * TILE;
-    uint16_t* Vs = Ks + TILE;
+    if (key0 + BN <= p.N) {
+      const uint16_t* t = base + (int64_t)key0 * stride;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int key = key0 + ld_row[i];
-      key = key < p.N ? key : p.N - 1;
-      const int off = (wave * LOADS + i) * 64 * 8;
-      g2lds16(kbase + (int64_t)key * p.ks_t + ld_col[i], Ks + off);
-      g2lds16(vbase + (int64_t)key * p.vs_t + ld_col[i], Vs + off);
+      for (int i = 0; i < LOADS; ++i) g2lds16(t + off[i], dst + (wave * LOADS + i) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int key = key0 + ld_row[i];
+        key = key < p.N ? key : p.N - 1;
+        g2lds16(base + (int64_t)key * stride + ld_col[i], dst + (wave * LOADS + i) * 512);
+      }
     }
   };
 
@@ -190,21 +199,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       v_off[ri][db] = key * D + (((d >> 3) ^ (key % CPR)) * 8) + (d & 7);
     }
 
-  if (e0 < e1) issue_loads(p.col[e0], 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Plan entries travel 64 at a time, one per lane (tile index with the
+  // full-tile flag in bit 31), and are picked out with readlane.
+  auto plan_chunk = [&](int base) {
+    const int e = base + lane;
+    return e < e1 ? (p.col[e] | (p.flags[e] ? (int)0x80000000 : 0)) : 0;
+  };
+  int pbase = e0;
+  int pchunk = plan_chunk(pbase);
+  auto entry = [&](int e) {  // requires pbase <= e < pbase + 64
+    return __builtin_amdgcn_readlane(pchunk, e - pbase);
+  };
 
-  for (int e = e0; e < e1; ++e) {
-    const int buf = (e - e0) & 1;
-    const int kj = p.col[e];
-    const bool full = p.flags[e] != 0;
-    if (e + 1 < e1) issue_loads(p.col[e + 1], buf ^ 1);
-
-    const uint16_t* Ks = smem + buf * 2 * TILE;
-    const uint16_t* Vs = Ks + TILE;
-
-    // S^T for keys [32*blk, 32*blk+32) of the tile
-    f32x16 s[2];
+  // S^T = K Q^T for the 64 keys of the K tile in buffer kb
+  auto qk = [&](const uint16_t* Ks, f32x16* s) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
@@ -214,15 +222,59 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[blk], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: iteration e holds S(e) in registers, reads K(e+1) and V(e) from
+  // LDS, and streams K(e+2) and V(e+1) into the buffers freed last iteration.
+  // The MFMAs of S(e+1) are independent of the softmax of S(e), so they
+  // overlap it.
+  f32x16 s_first[2];
+  int c_cur = 0, c_n1 = 0;  // plan entries of tiles e and e + 1
+  if (e0 < e1) {
+    c_cur = entry(e0);
+    c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
+    load_tile(kbase, p.ks_t, ld_koff, c_cur & 0x7fffffff, Kbuf);
+    load_tile(vbase, p.vs_t, ld_voff, c_cur & 0x7fffffff, Vbuf);
+    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, c_n1 & 0x7fffffff, Kbuf + TILE);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(Kbuf, s_first);
+    // every wave has read K(e0) before its buffer is refilled
+    __syncthreads();
+  }
+
+  // one pipeline step for tile e; s_cur holds S(e), s_nxt receives S(e+1)
+  auto step = [&](int e, f32x16* s_cur, f32x16* s_nxt) {
+    const int slot = (e - e0) & 1;
+    const int kj = c_cur & 0x7fffffff;
+    const bool full = c_cur < 0;
+    const bool has_next = e + 1 < e1;
+    // plan entry of tile e + 2 (the chunk moves on when e + 2 leaves it)
+    int c_n2 = 0;
+    if (e + 2 < e1) {
+      if (e + 2 - pbase == 64) {
+        pbase += 64;
+        pchunk = plan_chunk(pbase);
+      }
+      c_n2 = entry(e + 2);
+      load_tile(kbase, p.ks_t, ld_koff, c_n2 & 0x7fffffff, Kbuf + slot * TILE);
+    }
+    if (has_next) load_tile(vbase, p.vs_t, ld_voff, c_n1 & 0x7fffffff, Vbuf + (slot ^ 1) * TILE);
 
     if (!full) {
-      const int key0 = kj * BN + 4 * hl;
+      // branch-free form of the visibility predicate vis_g(t, j)
+      const int dist0 = q_row - (kj * BN + 4 * hl);
+      const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
+      const int sink_rel = hp.sink - (kj * BN + 4 * hl);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * blk + 8 * (i >> 2) + (i & 3);
-          if (!visible(hp, q_row, key)) s[blk][i] = NEG_INF;
+          const int o = 32 * blk + 8 * (i >> 2) + (i & 3);
+          const int dist = dist0 - o;
+          const bool win = (o < sink_rel) | (dist < hp.window) |
+                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
+          s_cur[blk][i] = ((dist >= 0) & win) ? s_cur[blk][i] : NEG_INF;
         }
     }
 
@@ -230,7 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s_cur[blk][i]);
     mt = pair_max(mt);
     // raise the reference maximum only where it grew past the threshold
     // (always on a row's first visible key: m_run = -inf gives +inf)
@@ -244,27 +296,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
       for (int i = 0; i < ND; ++i) acc[i] *= alpha;
     }
-
     const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
+
+    // ---- one basic block: S(e+1) MFMAs, softmax of S(e), P.V MFMAs ----
+    if (has_next) qk(Kbuf + (slot ^ 1) * TILE, s_nxt);
+    unsigned pk[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], p.scale_log2, -mb));
-        s[blk][i] = e2;
-        l_run += e2;
+      for (int i = 0; i < 8; ++i) {
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][2 * i], p.scale_log2, -mb));
+        const float c = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][2 * i + 1], p.scale_log2, -mb));
+        pk[blk][i] = pack_bf16(a, c);
+        l_run += a + c;
       }
-
-    // O^T += V^T P^T, four 16-key steps
+    const uint16_t* Vs = Vbuf + slot * TILE;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int blk = st >> 1;
-      const int o8 = (st & 1) * 8;
-      u32x4 pw;
-      pw.x = pack_bf16(s[blk][o8 + 0], s[blk][o8 + 1]);
-      pw.y = pack_bf16(s[blk][o8 + 2], s[blk][o8 + 3]);
-      pw.z = pack_bf16(s[blk][o8 + 4], s[blk][o8 + 5]);
-      pw.w = pack_bf16(s[blk][o8 + 6], s[blk][o8 + 7]);
+      const int o4 = (st & 1) * 4;
+      const u32x4 pw = {pk[blk][o4], pk[blk][o4 + 1], pk[blk][o4 + 2], pk[blk][o4 + 3]};
       const bf16x8 bv = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
@@ -275,9 +326,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
-
+    c_cur = c_n1;
+    c_n1 = c_n2;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  // unrolled by two so the two S register sets alternate without copies
+  f32x16 s_alt[2];
+  for (int e = e0; e < e1; e += 2) {
+    step(e, s_first, s_alt);
+    if (e + 1 < e1) step(e + 1, s_alt, s_first);
   }
 
   const float l_tot = pair_sum(l_run);
