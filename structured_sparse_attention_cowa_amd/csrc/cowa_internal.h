@@ -10,8 +10,8 @@
 
 namespace cowa {
 
-// Prefill kernel tile: 4 wavefronts x 32 query rows, 64 keys per K/V tile.
-constexpr int kFwdBlockM = 128;
+// Prefill kernel tile: 8 wavefronts x 32 query rows, 64 keys per K/V tile.
+constexpr int kFwdBlockM = 256;
 constexpr int kFwdBlockN = 64;
 
 // Decode: largest visible-key chunk one workgroup handles, and the largest

@@ -9,7 +9,8 @@
 // its global KV head).  Only the key tiles the plan lists are loaded; only
 // tiles the plan marks partial are masked.
 //
-// Workgroup = 4 wavefronts = 128 query rows of one (batch, query head).
+// Workgroup = 8 wavefronts = 256 query rows of one (batch, query head), so
+// every K/V tile staged in LDS serves 256 query rows.
 // Each wavefront owns 32 query rows and works in the transposed frame:
 //   S^T (32 keys x 32 queries) = K (32 x d) . Q^T (d x 32)     [MFMA 32x32x16]
 //   O^T (d x 32 queries)      += V^T (d x 64) . P^T (64 x 32)   [MFMA 32x32x16]
@@ -40,9 +41,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup
+constexpr int BM = kFwdBlockM;  // query rows per workgroup (32 per wavefront)
 constexpr int BN = kFwdBlockN;  // 64 keys per tile
-constexpr int NTHREADS = 256;
+constexpr int NWAVES = BM / 32;
+constexpr int NTHREADS = 64 * NWAVES;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
@@ -76,6 +78,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 // maximum is used for the sum and for the output).
 constexpr float RESCALE_LOG2 = 8.0f;
 
+#ifndef COWA_SCHED
+#define COWA_SCHED 1
+#endif
+
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   bf16x2 r = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(unsigned, r);
@@ -100,7 +106,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void cowa_fwd_kernel(FwdParams p) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
   constexpr int TILE = BN * D;                // bf16 elements per K or V tile
-  constexpr int LOADS = BN * CPR / 64 / 4;    // direct loads per wave per tile
+  constexpr int LOADS = BN * CPR / 64 / NWAVES;  // direct loads per wave per tile
+  static_assert(LOADS >= 1, "every wavefront loads part of each tile");
   constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
   constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
 
@@ -299,7 +306,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
 
     // ---- one basic block: S(e+1) MFMAs, softmax of S(e), P.V MFMAs ----
-    if (has_next) qk(Kbuf + (slot ^ 1) * TILE, s_nxt);
+    // (unconditional so that the scheduler can interleave it with the
+    // softmax; on a row's last tile it reads a stale buffer and is unused)
+    qk(Kbuf + (slot ^ 1) * TILE, s_nxt);
     unsigned pk[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -326,6 +335,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
+#if COWA_SCHED
+    // interleave: MFMAs of S(e+1) with the softmax VALU of S(e), then the
+    // P.V MFMAs with their transposed V reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+#if COWA_SCHED == 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#endif
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#endif
     c_cur = c_n1;
     c_n1 = c_n2;
     __builtin_amdgcn_s_waitcnt(0);

@@ -64,7 +64,7 @@ def compare_plan(cp, op, n, hkv, bm, bn, method="auto"):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("bm,bn", [(16, 16), (64, 64), (128, 64), (128, 128), (32, 48)])
+@pytest.mark.parametrize("bm,bn", [(16, 16), (64, 64), (128, 64), (128, 128), (256, 64), (32, 48)])
 @pytest.mark.parametrize("n,S,Wd,H,off,hkv", [
     (1024, 16, 128, 4, 0, 4),    # tiny workload, all heads
     (1000, 16, 128, 4, 1, 3),    # ragged, offset
@@ -83,6 +83,7 @@ def test_plan_bit_exact_small(lib, mode, bm, bn, n, S, Wd, H, off, hkv):
 @pytest.mark.parametrize("w", [W.P8K, W.P32K])
 def test_plan_bit_exact_workloads(lib, w):
     cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=w.h_kv_global)
+    compare_plan(cp, op, w.N, w.H_kv, 256, 64, method="fast")
     rp, col, fl = compare_plan(cp, op, w.N, w.H_kv, 128, 64, method="fast")
     if w is W.P8K:
         nqt = w.N // 128
@@ -101,7 +102,7 @@ def test_plan_8k_bruteforce_two_heads(lib):
 def test_plan_bit_exact_128k_rank(lib, g):
     w = W.P128K
     cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8, kv_head_offset=g)
-    compare_plan(cp, op, w.N, 1, 128, 64, method="fast")
+    compare_plan(cp, op, w.N, 1, 256, 64, method="fast")
 
 
 def test_plan_128k_causal_size(lib):
@@ -134,14 +135,15 @@ def test_plan_capacity_and_invalid(lib):
 
 
 def test_fwd_block_sizes(lib):
-    assert C.cowa_fwd_block_sizes(128) == (128, 64)
-    assert C.cowa_fwd_block_sizes(64) == (128, 64)
+    bm, bn = C.cowa_fwd_block_sizes(128)
+    assert (bm, bn) == C.cowa_fwd_block_sizes(64)
+    assert bm % 32 == 0 and bn == 64
     with pytest.raises(C.CowaError) as e:
         C.cowa_fwd_block_sizes(96)
     assert e.value.status == C.COWA_ERR_UNSUPPORTED
 
 
-def _fwd_raw(lib, cp, nnz=None, bm=128, bn=64, B=1, N=256, Hq=4, Hkv=2, d=128, scale=0.1,
+def _fwd_raw(lib, cp, nnz=None, bm=None, bn=None, B=1, N=256, Hq=4, Hkv=2, d=128, scale=0.1,
              o_dtype=0, null=None, strides=None):
     """Calls cowa_fwd with fake (never dereferenced) device pointers: every
     case here must be rejected on the host before any launch."""
@@ -149,8 +151,11 @@ def _fwd_raw(lib, cp, nnz=None, bm=128, bn=64, B=1, N=256, Hq=4, Hkv=2, d=128, s
     ptrs = {k: fake for k in ("rp", "col", "fl", "q", "k", "v", "o", "lse")}
     if null:
         ptrs[null] = None
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    bm = fbm if bm is None else bm
+    bn = fbn if bn is None else bn
     if nnz is None:
-        nnz = C.cowa_plan_size(cp, N, Hkv, 128, 64)
+        nnz = C.cowa_plan_size(cp, N, Hkv, fbm, fbn)
     s = strides if strides is not None else [1] * 12
     arr = (ctypes.c_int64 * 12)(*s)
     return lib.cowa_fwd(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, bm, bn,
@@ -163,6 +168,7 @@ def test_fwd_host_validation(lib):
     E = C
     assert _fwd_raw(lib, cp, nnz=3) == E.COWA_ERR_PLAN_MISMATCH
     assert _fwd_raw(lib, cp, bm=64) == E.COWA_ERR_UNSUPPORTED
+    assert _fwd_raw(lib, cp, bn=32) == E.COWA_ERR_UNSUPPORTED
     assert _fwd_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
     assert _fwd_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
     assert _fwd_raw(lib, cp, scale=0.0) == E.COWA_ERR_INVALID_ARG
@@ -176,8 +182,9 @@ def test_fwd_host_validation(lib):
     # a plan built for another window has another size
     cp4, _ = pat(n_ctx=4096, h_kv_global=2)
     cpw, _ = pat(n_ctx=4096, h_kv_global=2, window=64)
-    nnz_other = C.cowa_plan_size(cpw, 4096, 2, 128, 64)
-    assert nnz_other != C.cowa_plan_size(cp4, 4096, 2, 128, 64)
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    nnz_other = C.cowa_plan_size(cpw, 4096, 2, fbm, fbn)
+    assert nnz_other != C.cowa_plan_size(cp4, 4096, 2, fbm, fbn)
     assert _fwd_raw(lib, cp4, nnz=nnz_other, N=4096) == E.COWA_ERR_PLAN_MISMATCH
 
 
