@@ -45,6 +45,24 @@ def visible_counts(t, g, sink, window, band):
     return n
 
 
+def traffic_record(kernel: str, source: str):
+    """Calibrated HBM bytes per launch from the committed rocprofv3 summaries
+    (profiles/*.md), or None when the kernel source changed since then."""
+    import glob
+    import hashlib
+    digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic-record:"):
+                continue
+            f = dict(kv.split("=", 1) for kv in line.split()[1:])
+            if f.get("kernel") == kernel and f.get("source_sha256") == digest:
+                fb, wb = float(f["fetch_bytes"]), float(f["write_bytes"])
+                return {"bytes": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+                        "source": os.path.relpath(path, ROOT)}
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +227,9 @@ def main():
                                    "cowa_speedup": round(dec_causal_ms / dec_ms, 3)},
         }
 
+    tr_pre = traffic_record("cowa_fwd_kernel", "structured_sparse_attention_cowa_amd/csrc/fwd.hip")
+    tr_dec = traffic_record("cowa_decode_split",
+                            "structured_sparse_attention_cowa_amd/csrc/decode.hip")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wp, scale)
@@ -234,7 +255,9 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": tr_pre["bytes"] if tr_pre else None,
+                     "traffic_detail": tr_pre,
                      "kernel": "cowa_fwd_kernel<128,true>",
                      "algorithmic_flops_per_launch": flops[0]},
         "cpu_baseline": cpu,
@@ -243,7 +266,9 @@ def main():
         "decode": {"us": round(dec_ms * 1e3, 2), "tokens_per_s": round(dec_tps, 1),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": tr_dec["bytes"] if tr_dec else None,
+                                "traffic_detail": tr_dec,
                                 "algorithmic_bytes_per_step": dec_bytes}},
     }
     out.update(extras)
