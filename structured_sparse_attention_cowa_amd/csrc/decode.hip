@@ -17,7 +17,7 @@
 //            in fp32, reduced across lanes and wavefronts at the end.
 // The chunk's normalised output and log-sum-exp go to the workspace.
 // Combine kernel, one wavefront per (sequence, query head): merges the chunks
-// by their log-sum-exp.
+// by their log-sum-exp, all chunk statistics loaded in parallel.
 #include <hip/hip_runtime.h>
 
 #include "cowa_internal.h"
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   constexpr int LPV = D / 8;            // phase C: lanes per key
   constexpr int KPW = 64 / LPV;         // phase C: keys per wavefront step
   constexpr int UA = 2;                 // phase A unroll (keys per quad in flight)
-  constexpr int UC = 4;                 // phase C unroll
+  constexpr int UC = 8;                 // phase C unroll
 
   __shared__ __attribute__((aligned(16))) float sc[kDecodeChunkMax * GP];
   __shared__ float red[NWAVES][GP];
@@ -296,20 +296,45 @@ __global__ __launch_bounds__(64) void cowa_decode_combine(DecodeParams p) {
   const int64_t stride_s = (int64_t)p.B * p.Hq;
   const int64_t base = (int64_t)b * p.Hq + hq;
 
+  // chunk log-sum-exps: one per lane, wave-wide maximum
   float m = NEG_INF;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, p.lsepart[s * stride_s + base]);
+  for (int s = lane; s < ns; s += 64) m = fmaxf(m, p.lsepart[s * stride_s + base]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+
   constexpr int DPT = D / 64;  // dims per lane
   float o[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) o[i] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __expf(p.lsepart[s * stride_s + base] - m);
+  const float* op = p.opart + base * D + lane * DPT;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float w = s < ns ? __expf(p.lsepart[s * stride_s + base] - m) : 0.f;
     wsum += w;
-    const float* op = p.opart + (s * stride_s + base) * D;
+    const int n = ns - s0 < 64 ? ns - s0 : 64;
+    int k = 0;
+    for (; k + 4 <= n; k += 4) {
+      float v[4][DPT];
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(w, op[lane * DPT + i], o[i]);
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) v[u][i] = op[(s0 + k + u) * stride_s * D + i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wk = __shfl(w, k + u);
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wk, v[u][i], o[i]);
+      }
+    }
+    for (; k < n; ++k) {
+      const float wk = __shfl(w, k);
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wk, op[(s0 + k) * stride_s * D + i], o[i]);
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = 1.f / wsum;
   char* obase = reinterpret_cast<char*>(p.o);
   const int64_t oidx = (int64_t)b * p.os_b + (int64_t)hq * p.os_h + lane * DPT;
