@@ -23,8 +23,8 @@
 //
 // K and V tiles go from HBM straight into LDS (16 bytes per lane, no
 // register staging), row-major with the 16-byte chunks of each row XOR-
-// swizzled by the row index so that 16 consecutive rows read at one column
-// hit distinct banks.  K feeds the first product with 16-byte reads; V feeds
+// swizzled by a function of the row so that the reads below are free of
+// bank conflicts.  K feeds the first product with 16-byte reads; V feeds
 // the second through the gfx950 transposing read (ds_read_b64_tr_b16), which
 // hands each lane four keys of one head dimension.
 #include <hip/hip_runtime.h>
@@ -101,6 +101,19 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
 
+// LDS swizzles (16-byte chunk index XOR a function of the row), chosen so
+// that the reads below hit distinct banks whether the LDS serves 128 or 256
+// bytes per cycle.  K: 16 consecutive rows read one column chunk.  V: the
+// transposing read takes 4 consecutive keys x 2-4 adjacent chunks.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? ((((key & 3) << 2) ^ ((key & 3) << 1)) & 14) : (2 * (key & 3));
+}
+
 template <int D, bool OF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void cowa_fwd_kernel(FwdParams p) {
@@ -156,22 +169,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
 
   // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
-  // holds row P / CPR, column chunk (P % CPR) ^ (row % CPR).  Per-lane
+  // holds row P / CPR, column chunk (P % CPR) ^ swizzle(row).  Per-lane
   // offsets inside a tile are fixed; the tile base is uniform.
-  int ld_row[LOADS], ld_col[LOADS], ld_koff[LOADS], ld_voff[LOADS];
+  int ld_row[LOADS], ld_kcol[LOADS], ld_vcol[LOADS], ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
-    ld_col[i] = ((P % CPR) ^ (ld_row[i] % CPR)) * 8;
-    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_col[i];
-    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_col[i];
+    ld_kcol[i] = ((P % CPR) ^ kswz<D>(ld_row[i])) * 8;
+    ld_vcol[i] = ((P % CPR) ^ vswz<D>(ld_row[i])) * 8;
+    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_kcol[i];
+    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_vcol[i];
   }
   // Loads of one K (or V) tile into LDS buffer dst.  Keys past N (ragged last
   // tile) are clamped to N - 1: they only occur in tiles the plan marks
   // partial, where they are masked (probability exactly 0).
-  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, int kj,
-                       uint16_t* dst) {
+  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, const int* col,
+                       int kj, uint16_t* dst) {
     const int key0 = kj * BN;
     if (key0 + BN <= p.N) {
       const uint16_t* t = base + (int64_t)key0 * stride;
@@ -182,15 +196,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
         key = key < p.N ? key : p.N - 1;
-        g2lds16(base + (int64_t)key * stride + ld_col[i], dst + (wave * LOADS + i) * 512);
+        g2lds16(base + (int64_t)key * stride + col[i], dst + (wave * LOADS + i) * 512);
       }
     }
   };
 
   // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl
-  int k_off[NK];
+  int k_off[2][NK];
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) k_off[ks] = l32 * D + (((2 * ks + hl) ^ (l32 % CPR)) * 8);
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      k_off[blk][ks] = (32 * blk + l32) * D + (((2 * ks + hl) ^ kswz<D>(32 * blk + l32)) * 8);
   // V transposed-read offsets (second product, A operand): for 16-key step st,
   // d block db and half ri, lane reads key 16*st + 8*ri + 4*hl + (lane&15)/4 at
   // dims 32*db + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
@@ -203,7 +220,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     for (int db = 0; db < ND; ++db) {
       const int key = 8 * ri + 4 * hl + (r16 >> 2);
       const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
-      v_off[ri][db] = key * D + (((d >> 3) ^ (key % CPR)) * 8) + (d & 7);
+      v_off[ri][db] = key * D + (((d >> 3) ^ vswz<D>(key)) * 8) + (d & 7);
     }
 
   // Plan entries travel 64 at a time, one per lane (tile index with the
@@ -225,7 +242,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       s[blk] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + blk * 32 * D + k_off[ks]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + k_off[blk][ks]);
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[blk], 0, 0, 0);
       }
     }
@@ -240,9 +257,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   if (e0 < e1) {
     c_cur = entry(e0);
     c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
-    load_tile(kbase, p.ks_t, ld_koff, c_cur & 0x7fffffff, Kbuf);
-    load_tile(vbase, p.vs_t, ld_voff, c_cur & 0x7fffffff, Vbuf);
-    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, c_n1 & 0x7fffffff, Kbuf + TILE);
+    load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_cur & 0x7fffffff, Kbuf);
+    load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_cur & 0x7fffffff, Vbuf);
+    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n1 & 0x7fffffff, Kbuf + TILE);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(Kbuf, s_first);
@@ -264,9 +281,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pchunk = plan_chunk(pbase);
       }
       c_n2 = entry(e + 2);
-      load_tile(kbase, p.ks_t, ld_koff, c_n2 & 0x7fffffff, Kbuf + slot * TILE);
+      load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n2 & 0x7fffffff, Kbuf + slot * TILE);
     }
-    if (has_next) load_tile(vbase, p.vs_t, ld_voff, c_n1 & 0x7fffffff, Vbuf + (slot ^ 1) * TILE);
+    if (has_next) load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_n1 & 0x7fffffff, Vbuf + (slot ^ 1) * TILE);
 
     if (!full) {
       // branch-free form of the visibility predicate vis_g(t, j)
