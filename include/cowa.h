@@ -139,7 +139,7 @@ cowa_status cowa_fwd(const cowa_pattern* p,
  * 0..t_b; only those keys are read.  The same pattern as prefill is used, as
  * the pages require the pattern to be identical in training and inference
  * (Abstract).  The work is split over chunks of the visible keys of each
- * (b, KV head); a second kernel merges the chunks by their log-sum-exp.
+ * (b, KV head); a second kernel merges the chunks by log-sum-exp.
  *  q              bf16 [B, H_q, d], strides[0..1] (b, h)
  *  k_cache,v_cache bf16 [B, n_max, H_kv_local, d], strides[2..4], [5..7] (b,s,h)
  *  cache_seqlens  device int32[B], each in [1, n_max] (not checked on the
@@ -147,7 +147,9 @@ cowa_status cowa_fwd(const cowa_pattern* p,
  *  o              [B, H_q, d] of o_dtype, strides[8..9] (b, h)
  *  lse            fp32 [B, H_q], contiguous
  *  workspace      device scratch of at least cowa_decode_workspace_size bytes
- *                 (256-byte aligned), else COWA_ERR_WORKSPACE
+ *                 (256-byte aligned), else COWA_ERR_WORKSPACE; no
+ *                 initialisation needed.  Calls that share a workspace must
+ *                 not overlap (enqueue them on one stream).
  *  H_q / H_kv_local must be <= 8 (COWA_ERR_UNSUPPORTED otherwise). */
 cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,
                                        int32_t H_kv_local, int32_t d, int32_t n_max,

@@ -36,8 +36,9 @@ DecodeGeometry decode_geometry(const cowa_pattern* p, int32_t B, int32_t H_q, in
   if (chunk > kDecodeChunkMax) chunk = kDecodeChunkMax;
   g.chunk = (int32_t)chunk;
   g.n_splits = (int32_t)((max_vis + chunk - 1) / chunk);
-  g.opart_bytes = (size_t)g.n_splits * B * H_q * d * sizeof(float);
-  g.lse_offset = (g.opart_bytes + 255) / 256 * 256;
+  g.opart_offset = 0;
+  const size_t opart_bytes = (size_t)g.n_splits * B * H_q * d * sizeof(float);
+  g.lse_offset = g.opart_offset + (opart_bytes + 255) / 256 * 256;
   g.total_bytes = g.lse_offset + (size_t)g.n_splits * B * H_q * sizeof(float);
   return g;
 }
@@ -203,7 +204,7 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
   dp.seqlens = cache_seqlens;
   dp.o = o;
   dp.lse = lse;
-  dp.opart = static_cast<float*>(workspace);
+  dp.opart = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.opart_offset);
   dp.lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.lse_offset);
   dp.qs_b = strides[0]; dp.qs_h = strides[1];
   dp.ks_b = strides[2]; dp.ks_t = strides[3]; dp.ks_h = strides[4];
@@ -221,6 +222,7 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
   dp.causal = p->mode == COWA_MODE_CAUSAL;
   dp.chunk = geo.chunk;
   dp.n_splits = geo.n_splits;
+  dp.o_f32 = o_dtype == COWA_DTYPE_F32;
   dp.scale = softmax_scale;
   dp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_decode(dp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;

@@ -45,10 +45,12 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e)
 };
 
+// Decode workspace: partial outputs fp32[n_splits, B, H_q, d], then partial
+// LSEs fp32[n_splits, B, H_q].
 struct DecodeGeometry {
   int32_t chunk;     // visible keys per split
   int32_t n_splits;  // splits per (b, KV head), upper bound
-  size_t opart_bytes;
+  size_t opart_offset;
   size_t lse_offset;
   size_t total_bytes;
 };
@@ -72,6 +74,7 @@ struct DecodeParams {
   int32_t B, Hq, Hkv, G, n_max;
   int32_t sink, window, band, kv_head_offset, causal;
   int32_t chunk, n_splits;
+  int32_t o_f32;
   float scale;
   float scale_log2;
 };

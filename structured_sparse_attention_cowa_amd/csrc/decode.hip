@@ -8,16 +8,16 @@
 // concatenation in chunks, so only visible K/V rows are ever read.
 //
 // Split kernel, one workgroup per (chunk, KV head, sequence), 4 wavefronts:
-//   phase A  4 lanes per key (d/4 dims each) dot the key with all G query
-//            heads of the KV head (packed bf16 dot products, quad reduction)
-//            and store scaled scores in LDS;
+//   phase A  8 lanes per key (d/8 dims each) dot the key with all G query
+//            heads of the KV head (packed bf16 dot products, 8-lane DPP
+//            reduction) and store scaled scores in LDS;
 //   phase B  block max per head, then p = exp2(s - max) in LDS and the row
 //            sums;
 //   phase C  d/8 lanes per key (8 dims each) accumulate p * v for the G heads
 //            in fp32, reduced across lanes and wavefronts at the end.
 // The chunk's normalised output and log-sum-exp go to the workspace.
-// Combine kernel, one wavefront per (sequence, query head): merges the chunks
-// by their log-sum-exp, all chunk statistics loaded in parallel.
+// Combine kernel, one workgroup per (sequence, query head): merges the chunks
+// by their log-sum-exp, weights staged in LDS, partial loads all in flight.
 #include <hip/hip_runtime.h>
 
 #include "cowa_internal.h"
@@ -46,6 +46,32 @@ __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Cross-lane steps on the DPP path (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xb1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4e;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int DPP_ROR8 = 0x128;        // rotate by 8 within 16 lanes (= xor 8)
+
+// Sum over aligned groups of 8 lanes, result on every lane of the group.
+__device__ __forceinline__ float sum8(float a) {
+  a += dpp<DPP_XOR1>(a);
+  a += dpp<DPP_XOR2>(a);
+  return a + dpp<DPP_HALF_MIRROR>(a);
+}
+
+// Maximum over the wavefront of values that are uniform within 8-lane groups.
+__device__ __forceinline__ float wave_max_of_groups8(float m) {
+  m = fmaxf(m, dpp<DPP_ROR8>(m));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+}
 
 struct Segs {
   int lo0, n0, lo1, n1, lo2, n2;
@@ -78,12 +104,14 @@ __device__ __forceinline__ Segs decode_segs(const DecodeParams& p, int b, int h,
 template <int D, int G>
 __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   constexpr int GP = (G + 3) / 4 * 4;   // padded head count of an LDS score row
-  constexpr int DPL = D / 4;            // phase A: dims per lane
+  constexpr int LPA = 8;                // phase A: lanes per key
+  constexpr int KPA = 64 / LPA;         // phase A: keys per wavefront step
+  constexpr int DPL = D / LPA;          // phase A: dims per lane
   constexpr int NVA = DPL / 8;          // phase A: 16-byte loads per lane
   constexpr int LPV = D / 8;            // phase C: lanes per key
   constexpr int KPW = 64 / LPV;         // phase C: keys per wavefront step
-  constexpr int UA = 2;                 // phase A unroll (keys per quad in flight)
-  constexpr int UC = 8;                 // phase C unroll
+  constexpr int UA = 4;                 // phase A unroll (keys per lane group in flight)
+  constexpr int UC = 6;                 // phase C unroll
 
   __shared__ __attribute__((aligned(16))) float sc[kDecodeChunkMax * GP];
   __shared__ float red[NWAVES][GP];
@@ -110,8 +138,8 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
 
   // ---- phase A: scores ----
   {
-    const int quad = lane >> 2;
-    const int part = lane & 3;
+    const int quad = lane / LPA;   // key slot of this lane
+    const int part = lane % LPA;   // dims [part*DPL, (part+1)*DPL)
     u32x4 qr[G][NVA];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -123,11 +151,11 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) mx[hh] = NEG_INF;
 
-    for (int base = wave * 16 + quad; base < cnt; base += 64 * UA) {
+    for (int base = wave * KPA + quad; base < cnt; base += NWAVES * KPA * UA) {
       u32x4 kr[UA][NVA];
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
-        const int kk = base + 64 * u;
+        const int kk = base + NWAVES * KPA * u;
         if (kk < cnt) {
           const int key = sg.key(v0 + kk);
           const uint16_t* kp = kbase + (int64_t)key * p.ks_t + part * DPL;
@@ -137,7 +165,7 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
       }
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
-        const int kk = base + 64 * u;
+        const int kk = base + NWAVES * KPA * u;
         if (kk < cnt) {
           float sv[G];
 #pragma unroll
@@ -147,14 +175,13 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
             for (int i = 0; i < NVA; ++i)
 #pragma unroll
               for (int w = 0; w < 4; ++w) a = dot2(kr[u][i][w], qr[hh][i][w], a);
-            a += __shfl_xor(a, 1);
-            a += __shfl_xor(a, 2);
+            a = sum8(a);
             sv[hh] = a * p.scale_log2;
             mx[hh] = fmaxf(mx[hh], sv[hh]);
           }
 #pragma unroll
           for (int hh = 0; hh < G; ++hh)
-            if ((hh & 3) == part) sc[kk * GP + hh] = sv[hh];
+            if ((hh % LPA) == part) sc[kk * GP + hh] = sv[hh];
         }
       }
     }
@@ -162,10 +189,8 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float m = mx[hh];
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+#pragma unroll
+      for (int off = LPA; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
       if (lane == 0) red[wave][hh] = m;
     }
   }
@@ -284,74 +309,100 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   if (tid < G) p.lsepart[pidx + tid] = (stat_m[tid] + __log2f(stat_l[tid])) * LN2;
 }
 
-template <int D, bool OF32>
-__global__ __launch_bounds__(64) void cowa_decode_combine(DecodeParams p) {
+// Merge of the chunks of one (sequence, query head) by log-sum-exp.  The
+// chunk log-sum-exps are loaded one per thread, their weights kept in LDS;
+// four groups of 64 threads each sum a quarter of the chunks (all loads in
+// flight at once) and are added in LDS.
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void cowa_decode_combine(DecodeParams p) {
+  constexpr int MAXW = 1024;       // chunk weights held in LDS per pass
+  constexpr int DPT = D / 64;      // dims per thread
+  __shared__ float wts[MAXW];
+  __shared__ float red[NWAVES];
+  __shared__ __attribute__((aligned(16))) float part[NWAVES][D];
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int h = hq / p.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int t;
   const Segs sg = decode_segs(p, b, h, &t);
   const int ns = (sg.total() + p.chunk - 1) / p.chunk;
-  const int lane = threadIdx.x;
   const int64_t stride_s = (int64_t)p.B * p.Hq;
   const int64_t base = (int64_t)b * p.Hq + hq;
 
-  // chunk log-sum-exps: one per lane, wave-wide maximum
+  // maximum chunk log-sum-exp
   float m = NEG_INF;
-  for (int s = lane; s < ns; s += 64) m = fmaxf(m, p.lsepart[s * stride_s + base]);
+  for (int s2 = tid; s2 < ns; s2 += NTHREADS) m = fmaxf(m, p.lsepart[s2 * stride_s + base]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
 
-  constexpr int DPT = D / 64;  // dims per lane
   float o[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) o[i] = 0.f;
   float wsum = 0.f;
   const float* op = p.opart + base * D + lane * DPT;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    const float w = s < ns ? __expf(p.lsepart[s * stride_s + base] - m) : 0.f;
-    wsum += w;
-    const int n = ns - s0 < 64 ? ns - s0 : 64;
-    int k = 0;
-    for (; k + 4 <= n; k += 4) {
-      float v[4][DPT];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) v[u][i] = op[(s0 + k + u) * stride_s * D + i];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wk = __shfl(w, k + u);
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wk, v[u][i], o[i]);
-      }
+  for (int s0 = 0; s0 < ns; s0 += MAXW) {
+    const int nb = ns - s0 < MAXW ? ns - s0 : MAXW;
+    for (int i = tid; i < nb; i += NTHREADS) {
+      const float w = __expf(p.lsepart[(s0 + i) * stride_s + base] - M);
+      wts[i] = w;
+      wsum += w;
     }
-    for (; k < n; ++k) {
-      const float wk = __shfl(w, k);
+    __syncthreads();
+    // group `wave` takes chunks wave, wave + 4, ...
+    int k = wave;
+    for (; k + 4 * 7 < nb; k += 4 * 8) {
+      float v[8][DPT];
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wk, op[(s0 + k) * stride_s * D + i], o[i]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) v[u][i] = op[(int64_t)(s0 + k + 4 * u) * stride_s * D + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wts[k + 4 * u], v[u][i], o[i]);
     }
+    for (; k < nb; k += 4)
+#pragma unroll
+      for (int i = 0; i < DPT; ++i)
+        o[i] = __builtin_fmaf(wts[k], op[(int64_t)(s0 + k) * stride_s * D + i], o[i]);
+    __syncthreads();
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
-  const float inv = 1.f / wsum;
-  char* obase = reinterpret_cast<char*>(p.o);
-  const int64_t oidx = (int64_t)b * p.os_b + (int64_t)hq * p.os_h + lane * DPT;
+  if (lane == 0) red[wave] = wsum;
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) {
-    if (OF32)
-      reinterpret_cast<float*>(obase)[oidx + i] = o[i] * inv;
-    else
-      reinterpret_cast<__bf16*>(obase)[oidx + i] = (__bf16)(o[i] * inv);
+  for (int i = 0; i < DPT; ++i) part[wave][lane * DPT + i] = o[i];
+  __syncthreads();
+  const float W = red[0] + red[1] + red[2] + red[3];
+  if (wave == 0) {
+    char* obase = reinterpret_cast<char*>(p.o);
+    const int64_t oi = (int64_t)b * p.os_b + (int64_t)hq * p.os_h + lane * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      const int dd = lane * DPT + i;
+      const float v = (part[0][dd] + part[1][dd] + part[2][dd] + part[3][dd]) / W;
+      if (p.o_f32)
+        reinterpret_cast<float*>(obase)[oi + i] = v;
+      else
+        reinterpret_cast<__bf16*>(obase)[oi + i] = (__bf16)v;
+    }
+    if (lane == 0) p.lse[base] = M + __logf(W);
   }
-  if (lane == 0) p.lse[base] = m + __logf(wsum);
 }
 
 template <int D, int G>
 void launch_split(const DecodeParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.n_splits, (unsigned)p.Hkv, (unsigned)p.B);
   hipLaunchKernelGGL((cowa_decode_split<D, G>), grid, dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL((cowa_decode_combine<D>), dim3((unsigned)p.Hq, (unsigned)p.B),
+                     dim3(NTHREADS), 0, s, p);
 }
 
 template <int D>
@@ -373,19 +424,10 @@ int dispatch_group(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream) {
+  (void)o_f32;  // carried in p.o_f32
   hipStream_t s = static_cast<hipStream_t>(stream);
   int bad = d == 128 ? dispatch_group<128>(p, s) : dispatch_group<64>(p, s);
   if (bad) return (int)hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  const dim3 grid((unsigned)p.Hq, (unsigned)p.B);
-  if (d == 128) {
-    if (o_f32) hipLaunchKernelGGL((cowa_decode_combine<128, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((cowa_decode_combine<128, false>), grid, dim3(64), 0, s, p);
-  } else {
-    if (o_f32) hipLaunchKernelGGL((cowa_decode_combine<64, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((cowa_decode_combine<64, false>), grid, dim3(64), 0, s, p);
-  }
   return (int)hipGetLastError();
 }
 

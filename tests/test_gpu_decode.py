@@ -20,7 +20,7 @@ def run_decode(q_bits, k_dev, v_dev, lens, S, Wd, H, n_ctx, off=0, mode=0, o_dty
     n_max, Hkv = k_dev.shape[1], k_dev.shape[2]
     p = C.make_pattern(n_ctx, S, Wd, 0, H, off, mode)
     ws_bytes = C.cowa_decode_workspace_size(p, B, Hq, Hkv, d, n_max)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
     q = bits_to_dev(q_bits)
     odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
     o = torch.full((B, Hq, d), float("nan"), dtype=odt, device="cuda")
@@ -126,3 +126,30 @@ def test_decode_128k_workload_sampled(lib, mode):
         qf = W.bf16_bits_to_f32(q_bits[b:b + 1])
         o_ref, lse_ref = O.decode(qf, kb, vb, np.array([L]), p, 1.0 / np.sqrt(w.d))
         check_close(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, f"decode128k b={b} len={L}")
+
+
+def test_decode_reuses_workspace(lib):
+    """One workspace serves consecutive calls with different batches and
+    lengths; a repeated call reproduces its first result bit for bit."""
+    import torch
+    S, Wd, H, n_max, d = 16, 256, 4, 4096, 128
+    p = C.make_pattern(n_max, S, Wd, 0, H, 0, 0)
+    ws_bytes = C.cowa_decode_workspace_size(p, 4, 10, 2, d, n_max)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    results = []
+    for call, (B, seed) in enumerate([(4, 51), (3, 52), (4, 51)]):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        lens = rng.integers(1, n_max, endpoint=True, size=B).astype(np.int32)
+        q_bits = W.to_bf16_bits(rng.standard_normal((B, 10, d), dtype=np.float32))
+        kb, vb = W.decode_cache_host(seed + 1, B, n_max, 2, d, lens)
+        o = torch.empty((B, 10, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, 10), dtype=torch.float32, device="cuda")
+        C.cowa_decode(p, bits_to_dev(q_bits), bits_to_dev(kb), bits_to_dev(vb),
+                      torch.from_numpy(lens).cuda(), o, lse, 1.0 / np.sqrt(d), ws)
+        torch.cuda.synchronize()
+        op = O.Pattern(n_max, S, Wd, 0, H, 0, 0)
+        o_ref, lse_ref = O.decode(W.bf16_bits_to_f32(q_bits), W.bf16_bits_to_f32(kb),
+                                  W.bf16_bits_to_f32(vb), lens, op, 1.0 / np.sqrt(d))
+        check_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, f"reuse call {call}")
+        results.append(o.cpu().numpy())
+    assert np.array_equal(results[0], results[2])
