@@ -264,6 +264,20 @@ def tile_lists(n: int, h_kv_local: int, p: Pattern, bm: int, bn: int, method: st
     return _csr_from_counts(per_head, bm, bn)
 
 
+def tile_lists_kv(n: int, h_kv_local: int, p: Pattern, bm: int, bn: int, method: str = "auto"):
+    """Key-major visible-tile lists (for the backward pass over key tiles).
+
+    Rows of the CSR are ordered (h_local, kj); columns are the query tiles qi,
+    ascending; flags as in tile_lists (1 when all BM*BN elements are visible).
+    """
+    if method == "auto":
+        method = "bruteforce" if n <= 4096 else "fast"
+    fn = {"bruteforce": tile_counts_bruteforce, "intervals": tile_counts_intervals,
+          "fast": tile_counts_intervals_fast}[method]
+    per_head = [fn(n, p.kv_head_offset + h, p, bm, bn).T for h in range(h_kv_local)]
+    return _csr_from_counts(per_head, bm, bn)
+
+
 # --------------------------------------------------------------------------
 # Attention: dense masked softmax over each head's own visible set
 # ([SF] "What CoWA does not claim"), in float64.
@@ -357,3 +371,121 @@ def visible_pairs(n: int, g: int, p: Pattern) -> int:
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# --------------------------------------------------------------------------
+# Backward pass (the pages' training operator, [AB] Abstract: forward and
+# backward latency at 128K).  Gradients of sum(O * dO), i.e. the
+# vector-Jacobian product of the per-head masked softmax attention.
+#   P_tj  = exp(scale * s_tj - LSE_t) on the visible set, 0 elsewhere
+#   dV_j  = sum_t P_tj dO_t            (summed over the query heads of the group)
+#   dP_tj = dO_t . v_j
+#   D_t   = sum_c dO_tc O_tc           (= sum_j P_tj dP_tj)
+#   dS_tj = P_tj (dP_tj - D_t)
+#   dQ_t  = scale sum_j dS_tj k_j
+#   dK_j  = scale sum_t dS_tj q_t      (summed over the query heads of the group)
+# --------------------------------------------------------------------------
+
+
+def attention_backward(q, k, v, do, p: Pattern, scale: float):
+    """Full backward in float64 for moderate sizes (dense per head)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    t = np.arange(N)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            g = p.kv_head_offset + h
+            mask = visible(t[:, None], t[None, :], g, p)
+            s = (q[b, :, hq] @ k[b, :, h].T) * scale
+            s = np.where(mask, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+            P = np.exp(s - lse)
+            o = P @ v[b, :, h]
+            dP = do[b, :, hq] @ v[b, :, h].T
+            D = (do[b, :, hq] * o).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[b, :, hq] = scale * dS @ k[b, :, h]
+            dk[b, :, h] += scale * dS.T @ q[b, :, hq]
+            dv[b, :, h] += P.T @ do[b, :, hq]
+    return dq, dk, dv
+
+
+def backward_rows_dq(q, k, v, do, p: Pattern, scale: float, rows, heads=None):
+    """dQ for selected query rows only (each row needs only its own softmax)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    out = np.zeros((B, len(rows), len(heads), d))
+    for b in range(B):
+        for hi, hq in enumerate(heads):
+            h = hq // G
+            g = p.kv_head_offset + h
+            J = int(rows.max()) + 1
+            kk = np.asarray(k[b, :J, h], np.float64)
+            vv = np.asarray(v[b, :J, h], np.float64)
+            qq = np.asarray(q[b, rows, hq], np.float64)
+            dd = np.asarray(do[b, rows, hq], np.float64)
+            mask = visible(rows[:, None], np.arange(J)[None, :], g, p)
+            s = np.where(mask, (qq @ kk.T) * scale, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+            P = np.exp(s - lse)
+            o = P @ vv
+            dP = dd @ vv.T
+            D = (dd * o).sum(axis=1, keepdims=True)
+            out[b, :, hi] = scale * (P * (dP - D)) @ kk
+    return out
+
+
+def backward_keys_dkdv(q, k, v, do, p: Pattern, scale: float, keys, heads_kv=None):
+    """dK, dV for selected key positions: sums over every row that sees them
+    (practical for keys near the end of the sequence or at small N)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    heads_kv = list(range(Hkv)) if heads_kv is None else list(heads_kv)
+    dk = np.zeros((B, len(keys), len(heads_kv), d))
+    dv = np.zeros((B, len(keys), len(heads_kv), d))
+    for b in range(B):
+        for hi, h in enumerate(heads_kv):
+            g = p.kv_head_offset + h
+            # rows that can see any selected key
+            rows = np.arange(int(keys.min()), N)
+            vis_any = visible(rows[:, None], keys[None, :], g, p).any(axis=1)
+            rows = rows[vis_any]
+            if len(rows) == 0:
+                continue
+            J = int(rows.max()) + 1
+            kk = np.asarray(k[b, :J, h], np.float64)
+            vv = np.asarray(v[b, :J, h], np.float64)
+            for hq in range(h * G, (h + 1) * G):
+                for r0 in range(0, len(rows), 256):
+                    rt = rows[r0:r0 + 256]
+                    qq = np.asarray(q[b, rt, hq], np.float64)
+                    dd = np.asarray(do[b, rt, hq], np.float64)
+                    mask = visible(rt[:, None], np.arange(J)[None, :], g, p)
+                    s = np.where(mask, (qq @ kk.T) * scale, -np.inf)
+                    m = s.max(axis=1, keepdims=True)
+                    lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+                    P = np.exp(s - lse)
+                    o = P @ vv
+                    D = (dd * o).sum(axis=1, keepdims=True)
+                    Pk = P[:, keys]
+                    dPk = dd @ vv[keys].T
+                    dSk = Pk * (dPk - D)
+                    dk[b, :, hi] += scale * dSk.T @ qq
+                    dv[b, :, hi] += Pk.T @ dd
+    return dk, dv
