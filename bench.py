@@ -9,8 +9,9 @@ lengths uniform in [98304, 131072]).  Inputs are seeded synthetic data already
 resident in HBM.  Prints one JSON line.
 
 value = prefill tokens/s (B*N / prefill time).  The decode figures, the other
-seven global heads and the full-causal (FullAttn) mode sit in extra keys.
-Kernel times come from HIP events on the stream the library launches on.
+seven global heads, the full-causal (FullAttn) mode and the backward of the
+same prefill (training) sit in extra keys.  Kernel times come from HIP events
+on the stream the library launches on.
 """
 
 from __future__ import annotations
@@ -71,7 +72,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-head sweep and the full-causal comparison")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="profile a single kernel (rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -92,8 +94,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
             torch.bfloat16).to(dev)
 
-    need_prefill = args.only in (None, "prefill")
+    need_prefill = args.only in (None, "prefill", "backward")
     need_decode = args.only in (None, "decode")
+    need_backward = args.only == "backward" or (args.only is None and not args.no_backward)
 
     # ---------------- prefill setup ----------------
     wp = W.P128K
@@ -119,6 +122,27 @@ def main():
     def prefill(plan):
         p, rp, col, fl, nnz = plan
         C.cowa_fwd(p, rp, col, fl, nnz, bm, bn, q, k, v, o, lse, scale)
+
+    # ---------------- backward setup (same prefill, training) ----------------
+    if need_backward:
+        bmk, bnk = C.cowa_bwd_block_sizes(d)
+        dout = to_dev(W.grad_output(7, B, N, Hq, d))
+        dq = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=dev)
+        dk = torch.empty((B, N, Hkv, d), dtype=torch.bfloat16, device=dev)
+        dv = torch.empty((B, N, Hkv, d), dtype=torch.bfloat16, device=dev)
+        ws_b = torch.empty(C.cowa_bwd_workspace_size(B, Hq, N), dtype=torch.uint8, device=dev)
+
+    def make_plan_kv(plan):
+        p = plan[0]
+        rp, col, fl = C.cowa_plan_kv(p, N, Hkv, bmk, bnk)
+        return (torch.from_numpy(rp).to(dev), torch.from_numpy(col).to(dev),
+                torch.from_numpy(fl).to(dev), len(col))
+
+    def backward(plan, plan_kv):
+        p, rp, col, fl, nnz = plan
+        rpk, colk, flk, nnzk = plan_kv
+        C.cowa_bwd(p, rp, col, fl, nnz, bm, bn, rpk, colk, flk, nnzk, bmk, bnk, q, k, v, o,
+                   dout, lse, dq, dk, dv, scale, ws_b)
 
     t_all = np.arange(N)
     G = Hq // Hkv
@@ -156,11 +180,16 @@ def main():
             dst = torch.empty_like(src)
             for _ in range(args.steps):
                 dst.copy_(src)
+        if args.only == "backward":
+            plan_kv0 = make_plan_kv(plan0)
+            prefill(plan0)
         for _ in range(args.steps):
             if args.only == "prefill":
                 prefill(plan0)
             elif args.only == "decode":
                 decode()
+            elif args.only == "backward":
+                backward(plan0, plan_kv0)
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "steps": args.steps}))
         return
@@ -226,6 +255,34 @@ def main():
                                     "cowa_speedup_mean_g": round(causal_ms / np.mean(per_g), 3)},
             "decode_causal_mode": {"us": round(dec_causal_ms * 1e3, 2),
                                    "cowa_speedup": round(dec_causal_ms / dec_ms, 3)},
+        }
+
+    if need_backward:
+        # O and LSE of the forward at g = 0 feed the backward, as in training
+        plan_kv0 = make_plan_kv(plan0)
+        prefill(plan0)
+        bwd_ms = time_it(lambda: backward(plan0, plan_kv0), max(3, args.steps // 2))
+        causal_plan_b = make_plan(0, mode=1)
+        causal_kv = make_plan_kv(causal_plan_b)
+        prefill(causal_plan_b)
+        bwd_causal_ms = time_it(lambda: backward(causal_plan_b, causal_kv), 2)
+        prefill(plan0)
+        # dQ, dK, dV from S, P, dP, dS: five products of the visible pairs
+        # (the kernels recompute S and dP once more for dQ)
+        bwd_flops = 2.5 * flops[0]
+        bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+        extras["backward"] = {
+            "workload": "backward of the 128K single-rank prefill at g=0 (O fp32 from the "
+                        "forward, dO N(0,1) bf16, dQ/dK/dV bf16)",
+            "ms": round(bwd_ms, 4),
+            "tokens_per_s": round(B * N / (bwd_ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flops_per_call": bwd_flops},
+            "fwd_plus_bwd_ms": round(pre_ms + bwd_ms, 4),
+            "causal_mode_ms": round(bwd_causal_ms, 4),
+            "cowa_speedup_vs_causal": round(bwd_causal_ms / bwd_ms, 3),
         }
 
     tr_pre = traffic_record("cowa_fwd_kernel", "structured_sparse_attention_cowa_amd/csrc/fwd.hip")

@@ -161,6 +161,51 @@ cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cach
                         const int64_t strides[10], float softmax_scale,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- cowa_bwd: backward of the prefill (training) operator -------------
+ * The pages report the backward latency of the training operator next to
+ * the forward ("CoWindow Attention: Full Causal Coverage Is a Collective
+ * Property", Abstract).  Gradients of sum(O * dO) with
+ *   P_tj = exp(scale q_t.k_j - LSE_t) on vis_g(t), 0 elsewhere,
+ *   D_t = sum_c dO_tc O_tc,  dS_tj = P_tj (dO_t.v_j - D_t),
+ *   dQ_t = scale sum_j dS_tj k_j,
+ *   dK_j = scale sum_{t, hq in group} dS_tj q_t,  dV_j = sum_{t, hq} P_tj dO_t.
+ * Two plans of the same pattern are needed:
+ *   query-major: cowa_plan with cowa_fwd_block_sizes (the forward plan), for dQ;
+ *   key-major:   cowa_plan_kv with cowa_bwd_block_sizes, for dK and dV.
+ *  q, k, v, dout  bf16, layouts as in cowa_fwd (dout like q)
+ *  o              forward output [B, N, H_q, d] of o_dtype (bf16 or fp32)
+ *  lse            forward LSE fp32 [B, H_q, N]
+ *  dq             [B, N, H_q, d]; dk, dv [B, N, H_kv_local, d]; all of g_dtype
+ *  strides        element strides (b, t, h) of q, k, v, o, dout, dq, dk, dv (24)
+ *  workspace      device scratch of cowa_bwd_workspace_size bytes (256-byte
+ *                 aligned; no initialisation needed)
+ *  d              128 (COWA_ERR_UNSUPPORTED otherwise).
+ * Arithmetic: bf16 operands, fp32 accumulation; P and dS are rounded to bf16
+ * before their products. */
+cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n);
+
+/* Key-major visible-tile lists: rows r = h * nkt + kj (nkt = ceil(n/block_n)),
+ * columns the query tiles qi in ascending order, flags as in cowa_plan. */
+cowa_status cowa_plan_kv_size(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                              int32_t block_m, int32_t block_n, int64_t* nnz_out);
+cowa_status cowa_plan_kv(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                         int32_t block_m, int32_t block_n,
+                         int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t cap);
+
+cowa_status cowa_bwd_workspace_size(int32_t B, int32_t H_q, int32_t N, size_t* bytes);
+cowa_status cowa_bwd(const cowa_pattern* p,
+                     const int32_t* d_row_ptr, const int32_t* d_col, const uint8_t* d_flags,
+                     int64_t nnz, int32_t block_m, int32_t block_n,
+                     const int32_t* d_row_ptr_kv, const int32_t* d_col_kv,
+                     const uint8_t* d_flags_kv, int64_t nnz_kv, int32_t block_m_kv,
+                     int32_t block_n_kv,
+                     const void* q, const void* k, const void* v, const void* o,
+                     int32_t o_dtype, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int32_t g_dtype,
+                     int32_t B, int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
+                     const int64_t strides[24], float softmax_scale,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -387,8 +387,18 @@ def default_scale(d: int) -> float:
 # --------------------------------------------------------------------------
 
 
-def attention_backward(q, k, v, do, p: Pattern, scale: float):
-    """Full backward in float64 for moderate sizes (dense per head)."""
+def attention_backward(q, k, v, do, p: Pattern, scale: float, magnitudes: bool = False):
+    """Full backward in float64 for moderate sizes (dense per head).
+
+    With magnitudes=True it also returns, for each gradient, the sum of the
+    absolute values of the terms it is the sum of (scale sum_j |dS_tj| |k_j|,
+    scale sum_t |dS_tj| |q_t|, sum_t P_tj |dO_t|): the scale against which a
+    rounding error of each term is measured; and the sensitivities of dQ and
+    dK to an error in D_t of relative size 1 in every term of D's inputs:
+      w_t  = sum_c |dO_tc| (sum_j P_tj |v_jc| + |O_tc|)
+      eq_t = scale w_t sum_j P_tj |k_j|,  ek_j = scale sum_t P_tj w_t |q_t|.
+    (An O computed with relative errors u in P and stored with relative error
+    u moves D_t by at most u w_t.)  Returns dq, dk, dv, mq, mk, mv, eq, ek."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -399,6 +409,8 @@ def attention_backward(q, k, v, do, p: Pattern, scale: float):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    eq, ek = np.zeros_like(q), np.zeros_like(k)
     t = np.arange(N)
     for b in range(B):
         for hq in range(Hq):
@@ -417,17 +429,37 @@ def attention_backward(q, k, v, do, p: Pattern, scale: float):
             dq[b, :, hq] = scale * dS @ k[b, :, h]
             dk[b, :, h] += scale * dS.T @ q[b, :, hq]
             dv[b, :, h] += P.T @ do[b, :, hq]
+            if magnitudes:
+                aS = np.abs(dS)
+                mq[b, :, hq] = scale * aS @ np.abs(k[b, :, h])
+                mk[b, :, h] += scale * aS.T @ np.abs(q[b, :, hq])
+                mv[b, :, h] += P.T @ np.abs(do[b, :, hq])
+                w = _d_sensitivity(P, v[b, :, h], o, do[b, :, hq])
+                eq[b, :, hq] = scale * w[:, None] * (P @ np.abs(k[b, :, h]))
+                ek[b, :, h] += scale * P.T @ (w[:, None] * np.abs(q[b, :, hq]))
+    if magnitudes:
+        return dq, dk, dv, mq, mk, mv, eq, ek
     return dq, dk, dv
 
 
-def backward_rows_dq(q, k, v, do, p: Pattern, scale: float, rows, heads=None):
-    """dQ for selected query rows only (each row needs only its own softmax)."""
+def _d_sensitivity(P, v, o, do):
+    """w_t = sum_c |dO_tc| (sum_j P_tj |v_jc| + |O_tc|) for the rows of P."""
+    return (np.abs(do) * (P @ np.abs(v) + np.abs(o))).sum(axis=1)
+
+
+def backward_rows_dq(q, k, v, do, p: Pattern, scale: float, rows, heads=None,
+                     magnitudes: bool = False):
+    """dQ for selected query rows only (each row needs only its own softmax);
+    magnitudes=True also returns mq and eq (as in attention_backward) for
+    those rows."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
     rows = np.asarray(rows, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
     out = np.zeros((B, len(rows), len(heads), d))
+    mag = np.zeros_like(out)
+    esens = np.zeros_like(out)
     for b in range(B):
         for hi, hq in enumerate(heads):
             h = hq // G
@@ -446,12 +478,20 @@ def backward_rows_dq(q, k, v, do, p: Pattern, scale: float, rows, heads=None):
             dP = dd @ vv.T
             D = (dd * o).sum(axis=1, keepdims=True)
             out[b, :, hi] = scale * (P * (dP - D)) @ kk
+            if magnitudes:
+                mag[b, :, hi] = scale * np.abs(P * (dP - D)) @ np.abs(kk)
+                w = _d_sensitivity(P, vv, o, dd)
+                esens[b, :, hi] = scale * w[:, None] * (P @ np.abs(kk))
+    if magnitudes:
+        return out, mag, esens
     return out
 
 
-def backward_keys_dkdv(q, k, v, do, p: Pattern, scale: float, keys, heads_kv=None):
+def backward_keys_dkdv(q, k, v, do, p: Pattern, scale: float, keys, heads_kv=None,
+                       magnitudes: bool = False):
     """dK, dV for selected key positions: sums over every row that sees them
-    (practical for keys near the end of the sequence or at small N)."""
+    (practical for keys near the end of the sequence or at small N);
+    magnitudes=True also returns mk, mv and ek (as in attention_backward)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -459,6 +499,7 @@ def backward_keys_dkdv(q, k, v, do, p: Pattern, scale: float, keys, heads_kv=Non
     heads_kv = list(range(Hkv)) if heads_kv is None else list(heads_kv)
     dk = np.zeros((B, len(keys), len(heads_kv), d))
     dv = np.zeros((B, len(keys), len(heads_kv), d))
+    mk, mv, ek = np.zeros_like(dk), np.zeros_like(dv), np.zeros_like(dk)
     for b in range(B):
         for hi, h in enumerate(heads_kv):
             g = p.kv_head_offset + h
@@ -488,4 +529,11 @@ def backward_keys_dkdv(q, k, v, do, p: Pattern, scale: float, keys, heads_kv=Non
                     dSk = Pk * (dPk - D)
                     dk[b, :, hi] += scale * dSk.T @ qq
                     dv[b, :, hi] += Pk.T @ dd
+                    if magnitudes:
+                        mk[b, :, hi] += scale * np.abs(dSk).T @ np.abs(qq)
+                        mv[b, :, hi] += Pk.T @ np.abs(dd)
+                        w = _d_sensitivity(P, vv, o, dd)
+                        ek[b, :, hi] += scale * Pk.T @ (w[:, None] * np.abs(qq))
+    if magnitudes:
+        return dk, dv, mk, mv, ek
     return dk, dv

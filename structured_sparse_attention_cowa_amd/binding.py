@@ -29,7 +29,9 @@ COWA_DTYPE_BF16 = 0
 COWA_DTYPE_F32 = 1
 
 EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa_plan_size",
-            "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode")
+            "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode",
+            "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
+            "cowa_bwd_workspace_size", "cowa_bwd")
 
 
 class CowaError(RuntimeError):
@@ -87,6 +89,18 @@ def load():
     lib.cowa_decode.restype = ctypes.c_int
     lib.cowa_decode.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                 P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_bwd_block_sizes.restype = ctypes.c_int
+    lib.cowa_bwd_block_sizes.argtypes = [i32, P(i32), P(i32)]
+    lib.cowa_plan_kv_size.restype = ctypes.c_int
+    lib.cowa_plan_kv_size.argtypes = [pat, i32, i32, i32, i32, P(i64)]
+    lib.cowa_plan_kv.restype = ctypes.c_int
+    lib.cowa_plan_kv.argtypes = [pat, i32, i32, i32, i32, vp, vp, vp, i64]
+    lib.cowa_bwd_workspace_size.restype = ctypes.c_int
+    lib.cowa_bwd_workspace_size.argtypes = [i32, i32, i32, P(ctypes.c_size_t)]
+    lib.cowa_bwd.restype = ctypes.c_int
+    lib.cowa_bwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, i32, i32,
+                             vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
+                             i32, i32, i32, i32, i32, P(i64), f32, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -220,3 +234,73 @@ def cowa_decode(p: cowa_pattern, q, k_cache, v_cache, cache_seqlens, o, lse,
                             float(softmax_scale), workspace.data_ptr(), workspace.numel()
                             * workspace.element_size(), _stream_ptr(stream))
     _check(st, "cowa_decode")
+
+
+def cowa_bwd_block_sizes(d: int):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().cowa_bwd_block_sizes(d, ctypes.byref(bm), ctypes.byref(bn)),
+           "cowa_bwd_block_sizes")
+    return bm.value, bn.value
+
+
+def cowa_plan_kv_size(p: cowa_pattern, n: int, h_kv_local: int, block_m: int,
+                      block_n: int) -> int:
+    nnz = ctypes.c_int64()
+    _check(load().cowa_plan_kv_size(ctypes.byref(p), n, h_kv_local, block_m, block_n,
+                                    ctypes.byref(nnz)), "cowa_plan_kv_size")
+    return nnz.value
+
+
+def cowa_plan_kv(p: cowa_pattern, n: int, h_kv_local: int, block_m: int, block_n: int):
+    """Key-major lists: (row_ptr int32 [h_kv_local * nkt + 1], col int32, flags uint8)."""
+    nnz = cowa_plan_kv_size(p, n, h_kv_local, block_m, block_n)
+    nkt = -(-n // block_n)
+    row_ptr = np.zeros(h_kv_local * nkt + 1, dtype=np.int32)
+    col = np.zeros(max(nnz, 1), dtype=np.int32)
+    flags = np.zeros(max(nnz, 1), dtype=np.uint8)
+    _check(load().cowa_plan_kv(ctypes.byref(p), n, h_kv_local, block_m, block_n,
+                               row_ptr.ctypes.data, col.ctypes.data, flags.ctypes.data, nnz),
+           "cowa_plan_kv")
+    return row_ptr, col[:nnz], flags[:nnz]
+
+
+def cowa_bwd_workspace_size(B: int, H_q: int, N: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().cowa_bwd_workspace_size(B, H_q, N, ctypes.byref(n)), "cowa_bwd_workspace_size")
+    return n.value
+
+
+def cowa_bwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
+             row_ptr_kv, col_kv, flags_kv, nnz_kv: int, block_m_kv: int, block_n_kv: int,
+             q, k, v, o, dout, lse, dq, dk, dv, softmax_scale: float, workspace, stream=None):
+    """Backward.  q/dout/dq [B,N,H_q,d], k/v/dk/dv [B,N,H_kv,d], o the forward
+    output (bf16 or fp32), lse [B,H_q,N] fp32; dq, dk, dv share one dtype."""
+    import torch
+    for t in (q, k, v, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v, dout must be bfloat16 GPU tensors")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk, dv must share one dtype")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    for t in (k, v, dk, dv):
+        if tuple(t.shape) != (B, N, Hkv, d):
+            raise ValueError("k, v, dk, dv must be [B, N, H_kv, d]")
+    for t in (o, dout, dq):
+        if tuple(t.shape) != (B, N, Hq, d):
+            raise ValueError("o, dout, dq must be [B, N, H_q, d]")
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be [B, H_q, N]")
+    strides = (ctypes.c_int64 * 24)(*(sum((_strides(t, 3) for t in (q, k, v, o, dout, dq, dk,
+                                                                       dv)), [])))
+    st = load().cowa_bwd(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
+                         nnz, block_m, block_n, row_ptr_kv.data_ptr(), col_kv.data_ptr(),
+                         flags_kv.data_ptr(), nnz_kv, block_m_kv, block_n_kv, q.data_ptr(),
+                         k.data_ptr(), v.data_ptr(), o.data_ptr(), _o_dtype(o),
+                         dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), _o_dtype(dq), B, N, Hq, Hkv, d, strides,
+                         float(softmax_scale), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check(st, "cowa_bwd")

@@ -227,3 +227,123 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
   dp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_decode(dp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
 }
+
+extern "C" cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n) {
+  if (!block_m || !block_n) return COWA_ERR_INVALID_ARG;
+  if (d != 128) return COWA_ERR_UNSUPPORTED;
+  *block_m = kBwdBlockM;
+  *block_n = kBwdBlockN;
+  return COWA_OK;
+}
+
+namespace {
+// Workspace of the backward: LSE2 then D, each [B, H_q, npad] fp32.
+struct BwdGeometry {
+  int32_t npad;
+  size_t delta_offset, total_bytes;
+};
+BwdGeometry bwd_geometry(int32_t B, int32_t H_q, int32_t N) {
+  BwdGeometry g;
+  g.npad = (N + kBwdBlockM - 1) / kBwdBlockM * kBwdBlockM;
+  const size_t one = ((size_t)B * H_q * g.npad * sizeof(float) + 255) / 256 * 256;
+  g.delta_offset = one;
+  g.total_bytes = 2 * one;
+  return g;
+}
+}  // namespace
+
+extern "C" cowa_status cowa_bwd_workspace_size(int32_t B, int32_t H_q, int32_t N, size_t* bytes) {
+  if (!bytes || B < 1 || H_q < 1 || N < 1) return COWA_ERR_INVALID_ARG;
+  *bytes = bwd_geometry(B, H_q, N).total_bytes;
+  return COWA_OK;
+}
+
+extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
+                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                                int32_t block_m, int32_t block_n, const int32_t* d_row_ptr_kv,
+                                const int32_t* d_col_kv, const uint8_t* d_flags_kv,
+                                int64_t nnz_kv, int32_t block_m_kv, int32_t block_n_kv,
+                                const void* q, const void* k, const void* v, const void* o,
+                                int32_t o_dtype, const void* dout, const float* lse, void* dq,
+                                void* dk, void* dv, int32_t g_dtype, int32_t B, int32_t N,
+                                int32_t H_q, int32_t H_kv_local, int32_t d,
+                                const int64_t strides[24], float softmax_scale, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  cowa_status st = validate_pattern(p, H_kv_local);
+  if (st != COWA_OK) return st;
+  if (!d_row_ptr || !d_col || !d_flags || !d_row_ptr_kv || !d_col_kv || !d_flags_kv || !q ||
+      !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !strides)
+    return COWA_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || H_q < 1 || H_q % H_kv_local != 0) return COWA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
+  if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
+  if (g_dtype != COWA_DTYPE_BF16 && g_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 24)) return COWA_ERR_INVALID_ARG;
+  if (d != 128) return COWA_ERR_UNSUPPORTED;
+  if (block_m != kFwdBlockM || block_n != kFwdBlockN || block_m_kv != kBwdBlockM ||
+      block_n_kv != kBwdBlockN)
+    return COWA_ERR_UNSUPPORTED;
+  // per-lane offsets inside one 64-row tile are 32-bit
+  const int tile_strides[4] = {1, 4, 7, 13};  // q, k, v, dout row strides
+  for (int i : tile_strides)
+    if ((int64_t)64 * strides[i] >= (1LL << 31)) return COWA_ERR_UNSUPPORTED;
+  const int64_t nqt = (N + block_m - 1) / block_m;
+  const int64_t nkt_kv = (N + block_n_kv - 1) / block_n_kv;
+  if ((int64_t)B * nqt * H_q > 0x7fffffffLL || (int64_t)B * H_kv_local * nkt_kv > 0x7fffffffLL ||
+      B > 65535 || H_q > 65535)
+    return COWA_ERR_UNSUPPORTED;
+  int64_t want = 0;
+  st = plan_size_memo(p, N, H_kv_local, block_m, block_n, &want);
+  if (st != COWA_OK) return st;
+  if (want != nnz) return COWA_ERR_PLAN_MISMATCH;
+  // the key-major plan holds the same tiles as the query-major one of its shape
+  st = plan_size_memo(p, N, H_kv_local, block_m_kv, block_n_kv, &want);
+  if (st != COWA_OK) return st;
+  if (want != nnz_kv) return COWA_ERR_PLAN_MISMATCH;
+  const BwdGeometry geo = bwd_geometry(B, H_q, N);
+  if (!workspace || ws_bytes < geo.total_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return COWA_ERR_WORKSPACE;
+
+  BwdParams bp;
+  bp.row_ptr = d_row_ptr;
+  bp.col = d_col;
+  bp.flags = d_flags;
+  bp.row_ptr_kv = d_row_ptr_kv;
+  bp.col_kv = d_col_kv;
+  bp.flags_kv = d_flags_kv;
+  bp.q = static_cast<const uint16_t*>(q);
+  bp.k = static_cast<const uint16_t*>(k);
+  bp.v = static_cast<const uint16_t*>(v);
+  bp.o = o;
+  bp.dout = static_cast<const uint16_t*>(dout);
+  bp.lse = lse;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.lse2 = static_cast<float*>(workspace);
+  bp.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.delta_offset);
+  int64_t* const dst[24] = {&bp.qs_b,  &bp.qs_t,  &bp.qs_h,  &bp.ks_b,  &bp.ks_t,  &bp.ks_h,
+                            &bp.vs_b,  &bp.vs_t,  &bp.vs_h,  &bp.os_b,  &bp.os_t,  &bp.os_h,
+                            &bp.dos_b, &bp.dos_t, &bp.dos_h, &bp.dqs_b, &bp.dqs_t, &bp.dqs_h,
+                            &bp.dks_b, &bp.dks_t, &bp.dks_h, &bp.dvs_b, &bp.dvs_t, &bp.dvs_h};
+  for (int i = 0; i < 24; ++i) *dst[i] = strides[i];
+  bp.B = B;
+  bp.N = N;
+  bp.Hq = H_q;
+  bp.Hkv = H_kv_local;
+  bp.G = H_q / H_kv_local;
+  bp.nqt = (int32_t)nqt;
+  bp.nkt_kv = (int32_t)nkt_kv;
+  bp.nqt_kv = (N + block_m_kv - 1) / block_m_kv;
+  bp.npad = geo.npad;
+  bp.sink = p->sink;
+  bp.window = p->window;
+  bp.band = resolve_band(p);
+  bp.kv_head_offset = p->kv_head_offset;
+  bp.causal = p->mode == COWA_MODE_CAUSAL;
+  bp.o_f32 = o_dtype == COWA_DTYPE_F32;
+  bp.g_f32 = g_dtype == COWA_DTYPE_F32;
+  bp.scale = softmax_scale;
+  bp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launch_bwd(bp, d, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}

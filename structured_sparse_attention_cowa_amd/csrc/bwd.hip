@@ -1,0 +1,556 @@
+// CoWA prefill backward for gfx950 (CDNA4): dQ, dK, dV on the visible tiles
+// only, bf16 MFMA with fp32 accumulation.
+//
+// What is differentiated ("CoWindow Attention: Full Causal Coverage Is a
+// Collective Property", Abstract, training latency of the operator): for
+// each query head, O_t = sum_j P_tj v_j with P_tj = exp(scale q_t.k_j - LSE_t)
+// over that head's visible keys (sink, local window, its global KV head's
+// band).  With D_t = dO_t . O_t and dS_tj = P_tj (dO_t . v_j - D_t):
+//   dQ_t = scale sum_j dS_tj k_j
+//   dK_j = scale sum_{t, heads of the group} dS_tj q_t
+//   dV_j = sum_{t, heads of the group} P_tj dO_t
+// P is recomputed from the forward's LSE, so no probability matrix is stored.
+//
+// Three kernels on the caller's stream:
+//   delta  D_t and LSE in base-2 units into the workspace (rows padded to a
+//          multiple of 64; padding rows get LSE = +inf, so P = 0 there);
+//   dQ     one workgroup per (batch, query head, 256-row query tile), the
+//          forward's query-major plan.  Each wavefront owns 32 query rows in
+//          the transposed frame of the forward: S^T = K Q^T and dP^T = V dO^T
+//          (lane = query column, so LSE and D are per-lane scalars), then
+//          dQ^T += K^T dS^T with K read through the transposing LDS read;
+//   dK/dV  one workgroup per (batch, KV head, 128-key tile), the key-major
+//          plan.  Each wavefront owns 32 keys whose K and V rows stay in
+//          registers; for every query head of the group and every visible
+//          64-row query tile: S = Q K^T, dP = dO V^T (lane = key column), then
+//          dV^T += dO^T P and dK^T += Q^T dS with dO and Q read transposed.
+//          Summing the group's query heads inside the workgroup needs no
+//          atomics, and the result is deterministic.
+// Tiles stream from HBM straight into LDS (16 bytes per lane), double
+// buffered, with one swizzle that serves both the plain and the transposing
+// reads without bank conflicts.
+#include <hip/hip_runtime.h>
+
+#include "cowa_internal.h"
+#include "kernel_util.h"
+
+namespace cowa {
+namespace {
+
+using namespace kern;
+
+constexpr int D = 128;
+constexpr int CPR = D / 8;  // 16-byte chunks per row
+constexpr int NK = D / 16;  // 16-deep k steps over the head dimension
+constexpr int ND = D / 32;  // 32-wide head-dimension blocks of an accumulator
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- delta --
+constexpr int DELTA_ROWS = 16;  // 16 lanes per row, 8 head dims each
+
+__global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
+  const int tid = threadIdx.x;
+  const int sub = tid & 15;
+  const int t = blockIdx.x * DELTA_ROWS + (tid >> 4);
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  float acc = 0.f;
+  if (t < p.N) {
+    const u32x4 dw = ldg16(p.dout + (int64_t)b * p.dos_b + (int64_t)t * p.dos_t +
+                           (int64_t)hq * p.dos_h + 8 * sub);
+    const int64_t oi = (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)hq * p.os_h + 8 * sub;
+    float o[8];
+    if (p.o_f32) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + oi);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + oi + 4);
+      for (int e = 0; e < 4; ++e) {
+        o[e] = a[e];
+        o[4 + e] = c[e];
+      }
+    } else {
+      const u32x4 ow = ldg16(static_cast<const uint16_t*>(p.o) + oi);
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = bf_lo(ow[e]);
+        o[2 * e + 1] = bf_hi(ow[e]);
+      }
+    }
+    for (int e = 0; e < 4; ++e) acc += bf_lo(dw[e]) * o[2 * e] + bf_hi(dw[e]) * o[2 * e + 1];
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (sub == 0 && t < p.npad) {
+    const int64_t bh = (int64_t)b * p.Hq + hq;
+    p.delta[bh * p.npad + t] = t < p.N ? acc : 0.f;
+    p.lse2[bh * p.npad + t] = t < p.N ? p.lse[bh * p.N + t] * LOG2E : POS_INF;
+  }
+}
+
+// Offsets of the plain 16-byte reads of a swizzled [rows x 128] tile feeding
+// an A operand: row 32 blk + (lane % 32), chunk 2 ks + lane / 32.
+__device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][NK]) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      const int row = 32 * blk + l32;
+      off[blk][ks] = row * D + (((2 * ks + hl) ^ swz_both_d128(row)) * 8);
+    }
+}
+
+// Offsets of the transposing reads feeding an A operand whose k index runs
+// over 16 tile rows (add 16 D per step): half ri, head-dim block db; lane
+// addresses row 8 ri + 4 (lane / 32) + (lane % 16) / 4 at dims
+// 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3.
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][ND]) {
+  const int hl = lane >> 5, r16 = lane & 15, gi = (lane >> 4) & 1;
+#pragma unroll
+  for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int row = 8 * ri + 4 * hl + (r16 >> 2);
+      const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
+      off[ri][db] = row * D + (((d >> 3) ^ swz_both_d128(row)) * 8) + (d & 7);
+    }
+}
+
+// ------------------------------------------------------------------- dQ --
+constexpr int QBM = kFwdBlockM;  // 256 query rows per workgroup
+constexpr int QBN = kFwdBlockN;  // 64 keys per tile
+constexpr int QWAVES = QBM / 32;
+constexpr int QTHREADS = 64 * QWAVES;
+
+template <bool GF32>
+__global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
+                          amdgpu_waves_per_eu(2, 2))) void cowa_bwd_dq_kernel(BwdParams p) {
+  constexpr int TILE = QBN * D;
+  constexpr int LOADS = QBN * CPR / 64 / QWAVES;
+  static_assert(LOADS >= 1, "every wavefront loads part of each tile");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K[2], V[2]
+  uint16_t* const Kbuf = smem;
+  uint16_t* const Vbuf = smem + 2 * TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int per_b = p.nqt * p.Hq;
+  const int wg = blockIdx.x;
+  const int b = wg / per_b;
+  const int rem = wg - b * per_b;
+  const int qi = p.nqt - 1 - rem / p.Hq;  // heavy first
+  const int hq = rem - (rem / p.Hq) * p.Hq;
+  const int h = hq / p.G;
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+
+  const int q_row = qi * QBM + wave * 32 + l32;
+  const int q_row_c = q_row < p.N ? q_row : p.N - 1;
+  bf16x8 qf[NK], dof[NK];
+  {
+    const uint16_t* qp =
+        p.q + (int64_t)b * p.qs_b + (int64_t)q_row_c * p.qs_t + (int64_t)hq * p.qs_h;
+    const uint16_t* dp =
+        p.dout + (int64_t)b * p.dos_b + (int64_t)q_row_c * p.dos_t + (int64_t)hq * p.dos_h;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks + 8 * hl));
+      dof[ks] = __builtin_bit_cast(bf16x8, ldg16(dp + 16 * ks + 8 * hl));
+    }
+  }
+  const int64_t bh = (int64_t)b * p.Hq + hq;
+  const float lse2 = p.lse2[bh * p.npad + q_row_c];
+  const float dlt = p.delta[bh * p.npad + q_row_c];
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
+
+  const int row = h * p.nqt + qi;
+  const int e0 = p.row_ptr[row];
+  const int e1 = p.row_ptr[row + 1];
+  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
+  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+
+  int ld_row[LOADS], ld_col[LOADS], ld_koff[LOADS], ld_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (wave * LOADS + i) * 64 + lane;
+    ld_row[i] = P / CPR;
+    ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
+    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_col[i];
+    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_col[i];
+  }
+  // K and V tiles of key tile kj into buffer slot; keys past N (only in
+  // tiles the plan marks partial, where they are masked) are clamped.
+  auto load_kv = [&](int kj, int slot) {
+    const int key0 = kj * QBN;
+    uint16_t* kd = Kbuf + slot * TILE;
+    uint16_t* vd = Vbuf + slot * TILE;
+    if (key0 + QBN <= p.N) {
+      const uint16_t* kt = kbase + (int64_t)key0 * p.ks_t;
+      const uint16_t* vt = vbase + (int64_t)key0 * p.vs_t;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        g2lds16(kt + ld_koff[i], kd + (wave * LOADS + i) * 512);
+        g2lds16(vt + ld_voff[i], vd + (wave * LOADS + i) * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int key = key0 + ld_row[i];
+        key = key < p.N ? key : p.N - 1;
+        g2lds16(kbase + (int64_t)key * p.ks_t + ld_col[i], kd + (wave * LOADS + i) * 512);
+        g2lds16(vbase + (int64_t)key * p.vs_t + ld_col[i], vd + (wave * LOADS + i) * 512);
+      }
+    }
+  };
+
+  int n_off[2][NK], t_off[2][ND];
+  plain_offsets(l32, hl, n_off);
+  tr_offsets(lane, t_off);
+
+  auto entry = [&](int e) { return p.col[e] | (p.flags[e] ? (int)0x80000000 : 0); };
+
+  int c_cur = 0;
+  if (e0 < e1) {
+    c_cur = entry(e0);
+    load_kv(c_cur & 0x7fffffff, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int e = e0; e < e1; ++e) {
+    const int slot = (e - e0) & 1;
+    int c_nxt = 0;
+    if (e + 1 < e1) {
+      c_nxt = entry(e + 1);
+      load_kv(c_nxt & 0x7fffffff, slot ^ 1);
+    }
+    const int kj = c_cur & 0x7fffffff;
+    const bool full = c_cur < 0;
+    const uint16_t* Ks = Kbuf + slot * TILE;
+    const uint16_t* Vs = Vbuf + slot * TILE;
+
+    unsigned pk[2][8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16 s = f32x16{}, dpv = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + n_off[blk][ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + n_off[blk][ks]);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dof[ks], dpv, 0, 0, 0);
+      }
+      if (!full) {
+        // register i holds key kj*64 + 32 blk + 8 (i/4) + 4 hl + i%4
+        const int dist0 = q_row - (kj * QBN + 4 * hl);
+        const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
+        const int sink_rel = hp.sink - (kj * QBN + 4 * hl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o = 32 * blk + 8 * (i >> 2) + (i & 3);
+          const int dist = dist0 - o;
+          const bool win = (o < sink_rel) | (dist < hp.window) |
+                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
+          s[i] = ((dist >= 0) & win) ? s[i] : NEG_INF;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], p.scale_log2, -lse2));
+        const float p1 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], p.scale_log2, -lse2));
+        pk[blk][i] = pack_bf16(p0 * (dpv[2 * i] - dlt), p1 * (dpv[2 * i + 1] - dlt));
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int blk = st >> 1, o4 = (st & 1) * 4;
+      const u32x4 w = {pk[blk][o4], pk[blk][o4 + 1], pk[blk][o4 + 2], pk[blk][o4 + 3]};
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a =
+            lds_read_tr_pair(Ks + st * 16 * D + t_off[0][db], Ks + st * 16 * D + t_off[1][db]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
+      }
+    }
+    c_cur = c_nxt;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (q_row < p.N) {
+    char* gbase = reinterpret_cast<char*>(p.dq);
+    const int64_t gi = (int64_t)b * p.dqs_b + (int64_t)q_row * p.dqs_t + (int64_t)hq * p.dqs_h;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = 32 * db + 8 * g4 + 4 * hl;
+        const float v0 = acc[db][4 * g4] * p.scale, v1 = acc[db][4 * g4 + 1] * p.scale;
+        const float v2 = acc[db][4 * g4 + 2] * p.scale, v3 = acc[db][4 * g4 + 3] * p.scale;
+        if (GF32)
+          *reinterpret_cast<f32x4*>(gbase + (gi + dd) * 4) = f32x4{v0, v1, v2, v3};
+        else
+          *reinterpret_cast<u32x2*>(gbase + (gi + dd) * 2) =
+              u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK/dV --
+constexpr int KBM = kBwdBlockM;  // 64 query rows per step
+constexpr int KBN = kBwdBlockN;  // 128 keys per workgroup
+constexpr int KWAVES = KBN / 32;
+constexpr int KTHREADS = 64 * KWAVES;
+
+template <bool GF32>
+__device__ __forceinline__ void store_key_row(void* base, int64_t idx, const f32x16* acc,
+                                              float mul, int hl) {
+  char* g = reinterpret_cast<char*>(base);
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int dd = 32 * db + 8 * g4 + 4 * hl;
+      const float v0 = acc[db][4 * g4] * mul, v1 = acc[db][4 * g4 + 1] * mul;
+      const float v2 = acc[db][4 * g4 + 2] * mul, v3 = acc[db][4 * g4 + 3] * mul;
+      if (GF32)
+        *reinterpret_cast<f32x4*>(g + (idx + dd) * 4) = f32x4{v0, v1, v2, v3};
+      else
+        *reinterpret_cast<u32x2*>(g + (idx + dd) * 2) =
+            u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+    }
+}
+
+template <bool GF32>
+__global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
+                          amdgpu_waves_per_eu(1, 1))) void cowa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int TILE = KBM * D;
+  constexpr int LOADS = KBM * CPR / 64 / KWAVES;
+  static_assert(LOADS >= 1, "every wavefront loads part of each tile");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // Q[2], dO[2]
+  __shared__ __attribute__((aligned(16))) float stats[2][2][KBM];   // [slot][LSE2, D][row]
+  uint16_t* const Qbuf = smem;
+  uint16_t* const Obuf = smem + 2 * TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  // key tiles in ascending order: the early ones (sink, and in causal mode
+  // the longest columns) carry the most query tiles
+  const int per_kj = p.B * p.Hkv;
+  const int wg = blockIdx.x;
+  const int kj = wg / per_kj;
+  const int rem = wg - kj * per_kj;
+  const int b = rem / p.Hkv;
+  const int h = rem - b * p.Hkv;
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+
+  const int key = kj * KBN + wave * 32 + l32;
+  const int key_c = key < p.N ? key : p.N - 1;
+  bf16x8 kf[NK], vf[NK];
+  {
+    const uint16_t* kp = p.k + (int64_t)b * p.ks_b + (int64_t)key_c * p.ks_t + (int64_t)h * p.ks_h;
+    const uint16_t* vp = p.v + (int64_t)b * p.vs_b + (int64_t)key_c * p.vs_t + (int64_t)h * p.vs_h;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, ldg16(kp + 16 * ks + 8 * hl));
+      vf[ks] = __builtin_bit_cast(bf16x8, ldg16(vp + 16 * ks + 8 * hl));
+    }
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  const int r = h * p.nkt_kv + kj;
+  const int e0 = p.row_ptr_kv[r];
+  const int e1 = p.row_ptr_kv[r + 1];
+  const int nsteps = (e1 - e0) * p.G;
+
+  int ld_row[LOADS], ld_col[LOADS], ld_qoff[LOADS], ld_ooff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (wave * LOADS + i) * 64 + lane;
+    ld_row[i] = P / CPR;
+    ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
+    ld_qoff[i] = (int)(ld_row[i] * p.qs_t) + ld_col[i];
+    ld_ooff[i] = (int)(ld_row[i] * p.dos_t) + ld_col[i];
+  }
+  // Q and dO rows of query tile qi of head hq into buffer slot, with that
+  // tile's LSE2 and D; rows past N are clamped (their LSE2 is +inf).
+  auto load_q = [&](int hq, int qi, int slot) {
+    const int r0 = qi * KBM;
+    const uint16_t* qb = p.q + (int64_t)b * p.qs_b + (int64_t)hq * p.qs_h;
+    const uint16_t* ob = p.dout + (int64_t)b * p.dos_b + (int64_t)hq * p.dos_h;
+    uint16_t* qd = Qbuf + slot * TILE;
+    uint16_t* od = Obuf + slot * TILE;
+    if (r0 + KBM <= p.N) {
+      const uint16_t* qt = qb + (int64_t)r0 * p.qs_t;
+      const uint16_t* ot = ob + (int64_t)r0 * p.dos_t;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        g2lds16(qt + ld_qoff[i], qd + (wave * LOADS + i) * 512);
+        g2lds16(ot + ld_ooff[i], od + (wave * LOADS + i) * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int t = r0 + ld_row[i];
+        t = t < p.N ? t : p.N - 1;
+        g2lds16(qb + (int64_t)t * p.qs_t + ld_col[i], qd + (wave * LOADS + i) * 512);
+        g2lds16(ob + (int64_t)t * p.dos_t + ld_col[i], od + (wave * LOADS + i) * 512);
+      }
+    }
+    const int64_t so = ((int64_t)b * p.Hq + hq) * p.npad + r0;
+    if (wave == 0) g2lds4(p.lse2 + so + lane, &stats[slot][0][0]);
+    if (wave == 1) g2lds4(p.delta + so + lane, &stats[slot][1][0]);
+  };
+
+  int n_off[2][NK], t_off[2][ND];
+  plain_offsets(l32, hl, n_off);
+  tr_offsets(lane, t_off);
+
+  auto entry = [&](int e) { return p.col_kv[e] | (p.flags_kv[e] ? (int)0x80000000 : 0); };
+
+  // steps run over (query head of the group, visible query tile)
+  int hq_cur = h * p.G, e_cur = e0, c_cur = 0;
+  if (nsteps > 0) {
+    c_cur = entry(e0);
+    load_q(hq_cur, c_cur & 0x7fffffff, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
+  const bool key_sink = key < hp.sink;
+  for (int s = 0; s < nsteps; ++s) {
+    const int slot = s & 1;
+    int hq_nxt = hq_cur, e_nxt = e_cur + 1, c_nxt = 0;
+    if (e_nxt == e1) {
+      e_nxt = e0;
+      ++hq_nxt;
+    }
+    if (s + 1 < nsteps) {
+      c_nxt = entry(e_nxt);
+      load_q(hq_nxt, c_nxt & 0x7fffffff, slot ^ 1);
+    }
+    const int qi = c_cur & 0x7fffffff;
+    const bool full = c_cur < 0;
+    const uint16_t* Qs = Qbuf + slot * TILE;
+    const uint16_t* Os = Obuf + slot * TILE;
+    const float* sl = stats[slot][0];
+    const float* sd = stats[slot][1];
+
+    unsigned pp[2][8], ps[2][8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16 sv = f32x16{}, dpv = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs + n_off[blk][ks]);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sv, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Os + n_off[blk][ks]);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dpv, 0, 0, 0);
+      }
+      if (!full) {
+        // register i holds query qi*64 + 32 blk + 8 (i/4) + 4 hl + i%4
+        const int dist0 = qi * KBM + 4 * hl - key;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int dist = dist0 + 32 * blk + 8 * (i >> 2) + (i & 3);
+          const bool win = key_sink | (dist < hp.window) |
+                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
+          sv[i] = ((dist >= 0) & win) ? sv[i] : NEG_INF;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * blk + 8 * j + 4 * hl);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 32 * blk + 8 * j + 4 * hl);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pv[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * j + u], p.scale_log2, -l4[u]));
+          dsv[u] = pv[u] * (dpv[4 * j + u] - d4[u]);
+        }
+        pp[blk][2 * j] = pack_bf16(pv[0], pv[1]);
+        pp[blk][2 * j + 1] = pack_bf16(pv[2], pv[3]);
+        ps[blk][2 * j] = pack_bf16(dsv[0], dsv[1]);
+        ps[blk][2 * j + 1] = pack_bf16(dsv[2], dsv[3]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int blk = st >> 1, o4 = (st & 1) * 4;
+      const u32x4 wp = {pp[blk][o4], pp[blk][o4 + 1], pp[blk][o4 + 2], pp[blk][o4 + 3]};
+      const u32x4 ws = {ps[blk][o4], ps[blk][o4 + 1], ps[blk][o4 + 2], ps[blk][o4 + 3]};
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
+      const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a =
+            lds_read_tr_pair(Os + st * 16 * D + t_off[0][db], Os + st * 16 * D + t_off[1][db]);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, dv[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 a =
+            lds_read_tr_pair(Qs + st * 16 * D + t_off[0][db], Qs + st * 16 * D + t_off[1][db]);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, dk[db], 0, 0, 0);
+      }
+    }
+    hq_cur = hq_nxt;
+    e_cur = e_nxt;
+    c_cur = c_nxt;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (key < p.N) {
+    store_key_row<GF32>(p.dk,
+                        (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h, dk,
+                        p.scale, hl);
+    store_key_row<GF32>(p.dv,
+                        (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h, dv,
+                        1.f, hl);
+  }
+}
+
+}  // namespace
+
+int launch_bwd(const BwdParams& p, int d, void* stream) {
+  if (d != D) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(cowa_bwd_delta_kernel, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
+                     dim3(256), 0, s, p);
+  const dim3 gq((unsigned)((int64_t)p.B * p.nqt * p.Hq));
+  const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.nkt_kv));
+  if (p.g_f32) {
+    hipLaunchKernelGGL(cowa_bwd_dq_kernel<true>, gq, dim3(QTHREADS), 0, s, p);
+    hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<true>, gk, dim3(KTHREADS), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(cowa_bwd_dq_kernel<false>, gq, dim3(QTHREADS), 0, s, p);
+    hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<false>, gk, dim3(KTHREADS), 0, s, p);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace cowa

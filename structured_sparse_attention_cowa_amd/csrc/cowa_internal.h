@@ -79,8 +79,50 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Backward dK/dV kernel tile: 64 query rows x 128 keys (4 wavefronts x 32 keys).
+constexpr int kBwdBlockM = 64;
+constexpr int kBwdBlockN = 128;
+
+cowa_status plan_kv_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int32_t bm,
+                         int32_t bn, int32_t* row_ptr, int32_t* col, uint8_t* flags,
+                         int64_t cap, int64_t* nnz_out);
+
+struct BwdParams {
+  const int32_t* row_ptr;     // query-major plan (dQ)
+  const int32_t* col;
+  const uint8_t* flags;
+  const int32_t* row_ptr_kv;  // key-major plan (dK, dV)
+  const int32_t* col_kv;
+  const uint8_t* flags_kv;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* o;
+  const uint16_t* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse2;   // workspace [B, Hq, npad]: LSE * log2(e), +inf for rows >= N
+  float* delta;  // workspace [B, Hq, npad]: rowsum(dO * O), 0 for rows >= N
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int64_t dos_b, dos_t, dos_h;
+  int64_t dqs_b, dqs_t, dqs_h;
+  int64_t dks_b, dks_t, dks_h;
+  int64_t dvs_b, dvs_t, dvs_h;
+  int32_t B, N, Hq, Hkv, G, nqt, nkt_kv, nqt_kv, npad;
+  int32_t sink, window, band, kv_head_offset, causal;
+  int32_t o_f32, g_f32;
+  float scale;
+  float scale_log2;
+};
+
 // Launchers return a hipError_t value (0 on success).
 int launch_fwd(const FwdParams& p, int d, int o_f32, void* stream);
 int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream);
+int launch_bwd(const BwdParams& p, int d, void* stream);
 
 }  // namespace cowa

@@ -30,47 +30,17 @@
 #include <hip/hip_runtime.h>
 
 #include "cowa_internal.h"
+#include "kernel_util.h"
 
 namespace cowa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+using namespace kern;
 
 constexpr int BM = kFwdBlockM;  // query rows per workgroup (32 per wavefront)
 constexpr int BN = kFwdBlockN;  // 64 keys per tile
 constexpr int NWAVES = BM / 32;
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr float NEG_INF = -__builtin_huge_valf();
-
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Lane l and lane l^32 hold the two halves of one query column; this returns
-// (value of lane l, value of lane l^32) in some order on every lane.
-__device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float pair_max(float x) {
-  float a, b;
-  pair_swap(x, a, b);
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-  float a, b;
-  pair_swap(x, a, b);
-  return a + b;
-}
 
 // The running maximum is only raised when a row's maximum grows by more than
 // 2^RESCALE_LOG2 in probability terms; until then the stale maximum is kept
@@ -81,25 +51,6 @@ constexpr float RESCALE_LOG2 = 8.0f;
 #ifndef COWA_SCHED
 #define COWA_SCHED 1
 #endif
-
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  bf16x2 r = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(unsigned, r);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// One 16-byte chunk per lane from global memory straight into LDS; the
-// wavefront's 64 chunks land contiguously at lds_base (+16 bytes per lane).
-__device__ __forceinline__ void g2lds16(const uint16_t* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)lds_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-}
 
 // LDS swizzles (16-byte chunk index XOR a function of the row), chosen so
 // that the reads below hit distinct banks whether the LDS serves 128 or 256

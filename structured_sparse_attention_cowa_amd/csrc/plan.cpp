@@ -97,7 +97,63 @@ cowa_status plan_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int3
   return COWA_OK;
 }
 
+// Key-major lists: the query-major plan transposed per head (counting sort
+// over key tiles; query tiles stay ascending because they are visited in
+// order).
+cowa_status plan_kv_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int32_t bm,
+                         int32_t bn, int32_t* row_ptr, int32_t* col, uint8_t* flags,
+                         int64_t cap, int64_t* nnz_out) {
+  int64_t nnz = 0;
+  cowa_status st = plan_impl(p, n, h_kv_local, bm, bn, nullptr, nullptr, nullptr, 0, &nnz);
+  if (st != COWA_OK) return st;
+  if (nnz_out) *nnz_out = nnz;
+  if (!row_ptr) return COWA_OK;
+  if (nnz > cap) return COWA_ERR_CAPACITY;
+  const int32_t nqt = (n + bm - 1) / bm;
+  const int32_t nkt = (n + bn - 1) / bn;
+  std::vector<int32_t> qrp((size_t)h_kv_local * nqt + 1), qcol(nnz > 0 ? nnz : 1);
+  std::vector<uint8_t> qfl(nnz > 0 ? nnz : 1);
+  st = plan_impl(p, n, h_kv_local, bm, bn, qrp.data(), qcol.data(), qfl.data(), nnz, nullptr);
+  if (st != COWA_OK) return st;
+  std::vector<int64_t> fill(nkt);
+  row_ptr[0] = 0;
+  int64_t base = 0;
+  for (int32_t h = 0; h < h_kv_local; ++h) {
+    std::vector<int64_t> cnt(nkt, 0);
+    for (int64_t e = qrp[(size_t)h * nqt]; e < qrp[(size_t)(h + 1) * nqt]; ++e) ++cnt[qcol[e]];
+    for (int32_t kj = 0; kj < nkt; ++kj) {
+      fill[kj] = base;
+      base += cnt[kj];
+      row_ptr[(int64_t)h * nkt + kj + 1] = (int32_t)base;
+    }
+    for (int32_t qi = 0; qi < nqt; ++qi) {
+      const int64_t r = (int64_t)h * nqt + qi;
+      for (int64_t e = qrp[r]; e < qrp[r + 1]; ++e) {
+        const int64_t pos = fill[qcol[e]]++;
+        col[pos] = qi;
+        flags[pos] = qfl[e];
+      }
+    }
+  }
+  return COWA_OK;
+}
+
 }  // namespace cowa
+
+extern "C" cowa_status cowa_plan_kv_size(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                                         int32_t block_m, int32_t block_n, int64_t* nnz_out) {
+  if (!p || !nnz_out) return COWA_ERR_INVALID_ARG;
+  return cowa::plan_kv_impl(p, n, h_kv_local, block_m, block_n, nullptr, nullptr, nullptr, 0,
+                            nnz_out);
+}
+
+extern "C" cowa_status cowa_plan_kv(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
+                                    int32_t block_m, int32_t block_n, int32_t* row_ptr,
+                                    int32_t* col, uint8_t* flags, int64_t cap) {
+  if (!p || !row_ptr || (cap > 0 && (!col || !flags)) || cap < 0) return COWA_ERR_INVALID_ARG;
+  int64_t nnz = 0;
+  return cowa::plan_kv_impl(p, n, h_kv_local, block_m, block_n, row_ptr, col, flags, cap, &nnz);
+}
 
 extern "C" cowa_status cowa_plan_size(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
                                       int32_t block_m, int32_t block_n, int64_t* nnz_out) {

@@ -143,6 +143,12 @@ def random_prefill(seed, B, N, H_q, H_kv, d, scale_q=1.0):
     return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
 
 
+def grad_output(seed, B, N, H_q, d) -> np.ndarray:
+    """Upstream gradient dO for the backward: N(0,1), bf16 bits [B, N, H_q, d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return to_bf16_bits(rng.standard_normal((B, N, H_q, d), dtype=np.float32))
+
+
 def decode_lens(w: DecodeWorkload) -> np.ndarray:
     """Cached lengths, integers uniform on [len_lo, len_hi] (drawn first)."""
     rng = np.random.Generator(np.random.PCG64(w.seed))

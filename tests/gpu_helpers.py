@@ -12,6 +12,26 @@ from structured_sparse_attention_cowa_amd import workloads as W
 # Acceptance: O max-abs <= 2e-2; LSE |diff| <= 1e-3 * max(1, |LSE_ref|).
 O_TOL = 2e-2
 LSE_REL = 1e-3
+# Backward tolerance, element-wise, from the arithmetic of the kernels: every
+# gradient element is a sum of terms P_tj dO_t or scale dS_tj (k_j or q_t),
+# and the kernels round each P and dS once to bf16 (8-bit significand, unit
+# roundoff u = 2^-8) before an exact bf16 product and an fp32 sum.  D_t =
+# dO_t . O_t enters every dS_tj of a row with the same sign, so an error in O
+# (the forward's own bf16 rounding of P, and O's storage) moves dQ and dK by
+# up to that relative error times the oracle's D-sensitivities eq, ek.
+# Bounds:
+#   |err| <= GRAD_REL * m + D_REL_FWD * e   (O and LSE from the GPU forward)
+#   |err| <= GRAD_REL * m + D_REL_EXACT * e (O and LSE from the oracle: only
+#            fp32 rounding of O and fp32 sums remain in D and dP)
+# with m the sum of the terms' absolute values.  Each constant is twice the
+# rounding it covers: 2u = 2^-7 for bf16 roundings, and 2^-12 for fp32 sums of
+# 128 products (128 * 2^-24 = 2^-17) with room to spare.  A single-term sum
+# (a key seen by one row) can reach the full u, so the factor 2 is the only
+# headroom.  Gradients stored in bf16 add u |ref| (as 2u |ref|).
+GRAD_REL = 2.0 ** -7
+D_REL_FWD = 2.0 ** -7
+D_REL_EXACT = 2.0 ** -12
+OUT_REL_BF16 = 2.0 ** -7
 
 
 def check_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
@@ -80,3 +100,88 @@ def sample_rows(N, window, sink, band, h_kv_global, n_random, seed):
         edges += [base - 1, base, base + 1, base + 127, base + 128]
     r = np.concatenate([np.asarray(edges), rng.integers(0, N, n_random)])
     return np.unique(r[(r >= 0) & (r < N)])
+
+
+def check_grad(gpu, ref, m, e, what="", d_rel=D_REL_EXACT, out_rel=0.0):
+    """Element-wise |gpu - ref| <= GRAD_REL m + d_rel e (+ out_rel |ref| for
+    gradients stored in bf16).  Returns the largest ratio of error to bound."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite gradient"
+    if ref.size == 0:
+        return 0.0
+    bound = GRAD_REL * m + d_rel * e + out_rel * np.abs(ref) + 1e-30
+    ratio = np.abs(gpu - ref) / bound
+    worst = float(ratio.max())
+    i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert worst <= 1.0, (f"{what}: error {abs(gpu[i] - ref[i]):.3e} at {i} exceeds bound "
+                          f"{bound[i]:.3e} (ref {ref[i]:.3e}, m {m[i]:.3e}, e {e[i]:.3e})")
+    return worst
+
+
+class Backward:
+    """Device-resident backward problem: a Prefill (run first for O and LSE),
+    the upstream gradient, both plans, the workspace and the gradients."""
+
+    def __init__(self, x: W.PrefillInputs, sink, window, h_kv_global, offset=0, mode=0,
+                 n_ctx=None, o_dtype="f32", g_dtype="f32", do_seed=1):
+        import torch
+        self.pf = pf = Prefill(x, sink, window, h_kv_global, offset, mode, n_ctx, o_dtype)
+        B, N, Hq, Hkv, d = pf.B, pf.N, pf.Hq, pf.Hkv, pf.d
+        self.do_bits = W.grad_output(do_seed, B, N, Hq, d)
+        self.do = bits_to_dev(self.do_bits)
+        self.bm_kv, self.bn_kv = C.cowa_bwd_block_sizes(d)
+        rp, col, fl = C.cowa_plan_kv(pf.pattern, N, Hkv, self.bm_kv, self.bn_kv)
+        self.nnz_kv = len(col)
+        self.rp_kv = torch.from_numpy(rp).cuda()
+        self.col_kv = torch.from_numpy(col if len(col) else np.zeros(1, np.int32)).cuda()
+        self.fl_kv = torch.from_numpy(fl if len(fl) else np.zeros(1, np.uint8)).cuda()
+        self.ws = torch.empty(C.cowa_bwd_workspace_size(B, Hq, N), dtype=torch.uint8,
+                              device="cuda")
+        gdt = torch.float32 if g_dtype == "f32" else torch.bfloat16
+        self.dq = torch.full((B, N, Hq, d), float("nan"), dtype=gdt, device="cuda")
+        self.dk = torch.full((B, N, Hkv, d), float("nan"), dtype=gdt, device="cuda")
+        self.dv = torch.full((B, N, Hkv, d), float("nan"), dtype=gdt, device="cuda")
+
+    def run_bwd(self, stream=None):
+        pf = self.pf
+        C.cowa_bwd(pf.pattern, pf.rp, pf.col, pf.fl, pf.nnz, pf.bm, pf.bn, self.rp_kv,
+                   self.col_kv, self.fl_kv, self.nnz_kv, self.bm_kv, self.bn_kv, pf.q, pf.k,
+                   pf.v, pf.o, self.do, pf.lse, self.dq, self.dk, self.dv, pf.scale, self.ws,
+                   stream)
+
+    def run(self):
+        self.pf.run()
+        self.run_bwd()
+
+    def set_oracle_forward(self):
+        """Use the oracle's O and LSE (fp64 rounded to fp32) as the backward's
+        forward inputs, so that only the backward kernels' rounding remains."""
+        import torch
+        pf = self.pf
+        o, lse = pf.oracle()
+        pf.o = torch.from_numpy(o.astype(np.float32)).cuda()
+        pf.lse = torch.from_numpy(lse.astype(np.float32)).cuda()
+
+    def result(self):
+        import torch
+        torch.cuda.synchronize()
+        return (self.dq.float().cpu().numpy(), self.dk.float().cpu().numpy(),
+                self.dv.float().cpu().numpy())
+
+    def dout(self):
+        return W.bf16_bits_to_f32(self.do_bits)
+
+    def oracle_full(self):
+        x = self.pf.x
+        return O.attention_backward(x.q(), x.k(), x.v(), self.dout(), self.pf.opattern,
+                                    self.pf.scale, magnitudes=True)
+
+    def oracle_rows(self, rows, heads=None):
+        x = self.pf.x
+        return O.backward_rows_dq(x.q(), x.k(), x.v(), self.dout(), self.pf.opattern,
+                                  self.pf.scale, rows, heads, magnitudes=True)
+
+    def oracle_keys(self, keys, heads_kv=None):
+        x = self.pf.x
+        return O.backward_keys_dkdv(x.q(), x.k(), x.v(), self.dout(), self.pf.opattern,
+                                    self.pf.scale, keys, heads_kv, magnitudes=True)

@@ -1,0 +1,134 @@
+"""CPU tests of the backward's host side: the key-major plan (bit-exact against
+the oracle's own enumeration, transposed) and cowa_bwd's argument checks,
+which must reject every bad call before anything is launched."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle.cowa_oracle as O
+from structured_sparse_attention_cowa_amd import binding as C
+from structured_sparse_attention_cowa_amd import workloads as W
+
+
+def pat(**kw):
+    base = dict(n_ctx=1024, sink=16, window=128, band=0, h_kv_global=4, kv_head_offset=0, mode=0)
+    base.update(kw)
+    return C.make_pattern(**base), O.Pattern(**base)
+
+
+def compare_plan_kv(cp, op, n, hkv, bm, bn, method="auto"):
+    rp, col, fl = C.cowa_plan_kv(cp, n, hkv, bm, bn)
+    orp, ocol, ofl = O.tile_lists_kv(n, hkv, op, bm, bn, method=method)
+    assert np.array_equal(rp, orp)
+    assert np.array_equal(col, ocol)
+    assert np.array_equal(fl, ofl)
+    assert C.cowa_plan_kv_size(cp, n, hkv, bm, bn) == len(ocol)
+    # same tiles as the query-major plan of the same shape
+    assert C.cowa_plan_size(cp, n, hkv, bm, bn) == len(ocol)
+    return rp, col, fl
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("bm,bn", [(64, 128), (16, 16), (32, 48), (128, 64)])
+@pytest.mark.parametrize("n,S,Wd,H,off,hkv", [
+    (1024, 16, 128, 4, 0, 4),
+    (1000, 16, 128, 4, 1, 3),
+    (17, 2, 4, 4, 0, 4),
+    (333, 0, 1, 8, 5, 3),
+    (300, 7, 400, 4, 0, 4),
+    (129, 129, 1, 2, 0, 2),
+    (1, 0, 1, 1, 0, 1),
+])
+def test_plan_kv_bit_exact_small(lib, mode, bm, bn, n, S, Wd, H, off, hkv):
+    cp, op = pat(n_ctx=n, sink=S, window=Wd, h_kv_global=H, kv_head_offset=off, mode=mode)
+    compare_plan_kv(cp, op, n, hkv, bm, bn, method="bruteforce")
+
+
+@pytest.mark.parametrize("g", [0, 3, 7])
+def test_plan_kv_bit_exact_128k_rank(lib, g):
+    w = W.P128K
+    cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8, kv_head_offset=g)
+    bm, bn = C.cowa_bwd_block_sizes(128)
+    rp, col, fl = compare_plan_kv(cp, op, w.N, 1, bm, bn, method="fast")
+    # the sink tile is seen by every query tile
+    assert rp[1] - rp[0] == -(-w.N // bm)
+
+
+def test_plan_kv_8k_workload(lib):
+    w = W.P8K
+    cp, op = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=w.h_kv_global)
+    compare_plan_kv(cp, op, w.N, w.H_kv, 64, 128, method="fast")
+
+
+def test_bwd_block_sizes_and_workspace(lib):
+    bm, bn = C.cowa_bwd_block_sizes(128)
+    assert (bm, bn) == (64, 128)
+    with pytest.raises(C.CowaError) as e:
+        C.cowa_bwd_block_sizes(64)
+    assert e.value.status == C.COWA_ERR_UNSUPPORTED
+    # two fp32 arrays [B, H_q, N rounded up to 64], each 256-byte aligned
+    assert C.cowa_bwd_workspace_size(1, 1, 1) == 2 * 256
+    assert C.cowa_bwd_workspace_size(2, 5, 130) == 2 * (2 * 5 * 192 * 4)
+    with pytest.raises(C.CowaError):
+        C.cowa_bwd_workspace_size(0, 1, 1)
+
+
+def _bwd_raw(lib, cp, N=256, Hq=4, Hkv=2, d=128, B=1, nnz=None, nnz_kv=None, bm=None, bn=None,
+             bm_kv=None, bn_kv=None, scale=0.1, o_dtype=0, g_dtype=0, null=None, strides=None,
+             ws_ptr=0x100000, ws_bytes=None):
+    """cowa_bwd with fake (never dereferenced) device pointers."""
+    names = ("rp", "col", "fl", "rpk", "colk", "flk", "q", "k", "v", "o", "do", "lse", "dq",
+             "dk", "dv")
+    ptrs = {nm: ctypes.c_void_p(0x1000) for nm in names}
+    if null:
+        ptrs[null] = None
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    kbm, kbn = C.cowa_bwd_block_sizes(128)
+    bm = fbm if bm is None else bm
+    bn = fbn if bn is None else bn
+    bm_kv = kbm if bm_kv is None else bm_kv
+    bn_kv = kbn if bn_kv is None else bn_kv
+    if nnz is None:
+        nnz = C.cowa_plan_size(cp, N, Hkv, fbm, fbn)
+    if nnz_kv is None:
+        nnz_kv = C.cowa_plan_kv_size(cp, N, Hkv, kbm, kbn)
+    if ws_bytes is None:
+        ws_bytes = C.cowa_bwd_workspace_size(B, Hq, N)
+    arr = (ctypes.c_int64 * 24)(*(strides if strides is not None else [8] * 24))
+    P = ptrs
+    return lib.cowa_bwd(ctypes.byref(cp), P["rp"], P["col"], P["fl"], nnz, bm, bn, P["rpk"],
+                        P["colk"], P["flk"], nnz_kv, bm_kv, bn_kv, P["q"], P["k"], P["v"],
+                        P["o"], o_dtype, P["do"], P["lse"], P["dq"], P["dk"], P["dv"], g_dtype,
+                        B, N, Hq, Hkv, d, arr, scale, ctypes.c_void_p(ws_ptr) if ws_ptr else None,
+                        ws_bytes, None)
+
+
+def test_bwd_host_validation(lib):
+    cp, _ = pat(n_ctx=256, h_kv_global=2)
+    E = C
+    assert _bwd_raw(lib, cp, nnz=1) == E.COWA_ERR_PLAN_MISMATCH
+    assert _bwd_raw(lib, cp, nnz_kv=1) == E.COWA_ERR_PLAN_MISMATCH
+    assert _bwd_raw(lib, cp, bm=128) == E.COWA_ERR_UNSUPPORTED
+    assert _bwd_raw(lib, cp, bn_kv=64) == E.COWA_ERR_UNSUPPORTED
+    assert _bwd_raw(lib, cp, d=64) == E.COWA_ERR_UNSUPPORTED
+    assert _bwd_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, scale=float("inf")) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, o_dtype=5) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, g_dtype=5) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, strides=[8] * 23 + [-8]) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, strides=[8, 1 << 25] + [8] * 22) == E.COWA_ERR_UNSUPPORTED
+    for nm in ("rp", "col", "fl", "rpk", "colk", "flk", "q", "k", "v", "o", "do", "lse", "dq",
+               "dk", "dv"):
+        assert _bwd_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
+    ws = C.cowa_bwd_workspace_size(1, 4, 256)
+    assert _bwd_raw(lib, cp, ws_bytes=ws - 1) == E.COWA_ERR_WORKSPACE
+    assert _bwd_raw(lib, cp, ws_ptr=0) == E.COWA_ERR_WORKSPACE
+    assert _bwd_raw(lib, cp, ws_ptr=0x100040) == E.COWA_ERR_WORKSPACE
+    # a key-major plan of another window has another size
+    cp4, _ = pat(n_ctx=4096, h_kv_global=2)
+    cpw, _ = pat(n_ctx=4096, h_kv_global=2, window=64)
+    other = C.cowa_plan_kv_size(cpw, 4096, 2, 64, 128)
+    assert other != C.cowa_plan_kv_size(cp4, 4096, 2, 64, 128)
+    assert _bwd_raw(lib, cp4, N=4096, nnz_kv=other) == E.COWA_ERR_PLAN_MISMATCH

@@ -130,3 +130,52 @@ def test_kv_tile_lists_are_the_transpose():
             for e in range(rpt[r], rpt[r + 1]):
                 bt[(int(colt[e]), kj)] = int(flt[e])
         assert a == bt
+
+
+def test_backward_magnitudes():
+    """The term-magnitude sums bound each gradient (triangle inequality), equal
+    it when every term has one sign (dV with dO >= 0 is sum_t P_tj dO_t, all
+    terms >= 0), and the sampled forms return the same magnitudes."""
+    B, N, Hq, Hkv, d = 1, 200, 4, 2, 8
+    x = W.random_prefill(10, B, N, Hq, Hkv, d)
+    q, k, v = x.q(), x.k(), x.v()
+    rng = np.random.Generator(np.random.PCG64(11))
+    do = rng.standard_normal(q.shape)
+    p = Pattern(n_ctx=N, sink=4, window=20, h_kv_global=4, kv_head_offset=1)
+    dq, dk, dv, mq, mk, mv, eq, ek = O.attention_backward(q, k, v, do, p, 0.3,
+                                                          magnitudes=True)
+    for g, m in ((dq, mq), (dk, mk), (dv, mv)):
+        assert (m >= np.abs(g) - 1e-12).all()
+        assert (m > np.abs(g) + 1e-6).any()  # signs do cancel somewhere
+    assert (eq > 0).all() and (ek[:, :N] > 0).all()
+    do_pos = np.abs(do)
+    _, _, dv_p, _, _, mv_p, _, _ = O.attention_backward(q, k, v, do_pos, p, 0.3,
+                                                        magnitudes=True)
+    np.testing.assert_allclose(mv_p, dv_p, rtol=1e-13, atol=0)
+    rows = np.array([0, 5, 99, 199])
+    dq_s, mq_s, eq_s = O.backward_rows_dq(q, k, v, do, p, 0.3, rows, magnitudes=True)
+    np.testing.assert_allclose(mq_s, mq[:, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(eq_s, eq[:, rows], rtol=1e-12, atol=0)
+    keys = np.array([0, 3, 150, 199])
+    _, _, mk_s, mv_s, ek_s = O.backward_keys_dkdv(q, k, v, do, p, 0.3, keys, magnitudes=True)
+    np.testing.assert_allclose(mk_s, mk[:, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mv_s, mv[:, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ek_s, ek[:, keys], rtol=1e-12, atol=0)
+
+
+def test_backward_invariant_to_a_common_shift_of_v():
+    """Adding one vector c to every value row moves O_t and dP_tj by dO_t.c
+    and D_t by the same amount, so dS, dQ and dK do not change; dV does not
+    depend on V.  A dropped or mis-signed D term breaks this."""
+    B, N, Hq, Hkv, d = 1, 60, 4, 2, 8
+    x = W.random_prefill(12, B, N, Hq, Hkv, d)
+    q, k, v = x.q(), x.k(), x.v()
+    rng = np.random.Generator(np.random.PCG64(13))
+    do = rng.standard_normal(q.shape)
+    p = Pattern(n_ctx=N, sink=2, window=6, h_kv_global=2)
+    c = 3.0 * rng.standard_normal(d)
+    a = O.attention_backward(q, k, v, do, p, 0.5)
+    b = O.attention_backward(q, k, v + c, do, p, 0.5)
+    for u, w in zip(a, b):
+        np.testing.assert_allclose(u, w, rtol=0, atol=1e-11)
+    assert np.abs(a[0]).max() > 0.1
