@@ -130,7 +130,10 @@ def main():
         dq = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=dev)
         dk = torch.empty((B, N, Hkv, d), dtype=torch.bfloat16, device=dev)
         dv = torch.empty((B, N, Hkv, d), dtype=torch.bfloat16, device=dev)
-        ws_b = torch.empty(C.cowa_bwd_workspace_size(B, Hq, N), dtype=torch.uint8, device=dev)
+        ws_bytes = max(C.cowa_bwd_workspace_size(C.make_pattern(N, wp.sink, wp.window, 0,
+                                                                wp.h_kv_global, 0, mode),
+                                                 B, Hq, Hkv, N) for mode in (0, 1))
+        ws_b = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def make_plan_kv(plan):
         p = plan[0]

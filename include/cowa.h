@@ -192,7 +192,11 @@ cowa_status cowa_plan_kv(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
                          int32_t block_m, int32_t block_n,
                          int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t cap);
 
-cowa_status cowa_bwd_workspace_size(int32_t B, int32_t H_q, int32_t N, size_t* bytes);
+/* Workspace bytes of cowa_bwd for this pattern and shape (LSE and D per
+ * query row, plus fp32 partial dK/dV of the key tiles holding sink keys,
+ * whose work is split over several workgroups). */
+cowa_status cowa_bwd_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,
+                                    int32_t H_kv_local, int32_t N, size_t* bytes);
 cowa_status cowa_bwd(const cowa_pattern* p,
                      const int32_t* d_row_ptr, const int32_t* d_col, const uint8_t* d_flags,
                      int64_t nnz, int32_t block_m, int32_t block_n,

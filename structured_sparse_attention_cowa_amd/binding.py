@@ -96,7 +96,7 @@ def load():
     lib.cowa_plan_kv.restype = ctypes.c_int
     lib.cowa_plan_kv.argtypes = [pat, i32, i32, i32, i32, vp, vp, vp, i64]
     lib.cowa_bwd_workspace_size.restype = ctypes.c_int
-    lib.cowa_bwd_workspace_size.argtypes = [i32, i32, i32, P(ctypes.c_size_t)]
+    lib.cowa_bwd_workspace_size.argtypes = [pat, i32, i32, i32, i32, P(ctypes.c_size_t)]
     lib.cowa_bwd.restype = ctypes.c_int
     lib.cowa_bwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, i32, i32,
                              vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
@@ -264,9 +264,10 @@ def cowa_plan_kv(p: cowa_pattern, n: int, h_kv_local: int, block_m: int, block_n
     return row_ptr, col[:nnz], flags[:nnz]
 
 
-def cowa_bwd_workspace_size(B: int, H_q: int, N: int) -> int:
+def cowa_bwd_workspace_size(p: cowa_pattern, B: int, H_q: int, H_kv_local: int, N: int) -> int:
     n = ctypes.c_size_t()
-    _check(load().cowa_bwd_workspace_size(B, H_q, N, ctypes.byref(n)), "cowa_bwd_workspace_size")
+    _check(load().cowa_bwd_workspace_size(ctypes.byref(p), B, H_q, H_kv_local, N,
+                                          ctypes.byref(n)), "cowa_bwd_workspace_size")
     return n.value
 
 

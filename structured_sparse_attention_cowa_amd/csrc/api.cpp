@@ -237,24 +237,50 @@ extern "C" cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t
 }
 
 namespace {
-// Workspace of the backward: LSE2 then D, each [B, H_q, npad] fp32.
+// Workspace of the backward: LSE2 and D, each [B, H_q, npad] fp32, then the
+// fp32 dK/dV partials of the key tiles that hold sink keys.  Those tiles are
+// seen by every query tile, so their step lists (query heads x query tiles)
+// are cut into nch parts when they exceed twice the mean step count of a key
+// tile; the parts run as separate workgroups and a reduction sums them in a
+// fixed order.
 struct BwdGeometry {
-  int32_t npad;
-  size_t delta_offset, total_bytes;
+  int32_t npad, n_sink_tiles, nch;
+  size_t delta_offset, part_offset, total_bytes;
 };
-BwdGeometry bwd_geometry(int32_t B, int32_t H_q, int32_t N) {
-  BwdGeometry g;
-  g.npad = (N + kBwdBlockM - 1) / kBwdBlockM * kBwdBlockM;
-  const size_t one = ((size_t)B * H_q * g.npad * sizeof(float) + 255) / 256 * 256;
-  g.delta_offset = one;
-  g.total_bytes = 2 * one;
-  return g;
+cowa_status bwd_geometry(const cowa_pattern* p, int32_t B, int32_t H_q, int32_t H_kv_local,
+                         int32_t N, BwdGeometry* g) {
+  g->npad = (N + kBwdBlockM - 1) / kBwdBlockM * kBwdBlockM;
+  const size_t one = ((size_t)B * H_q * g->npad * sizeof(float) + 255) / 256 * 256;
+  g->delta_offset = one;
+  g->part_offset = 2 * one;
+  const int32_t nkt = (N + kBwdBlockN - 1) / kBwdBlockN;
+  const int32_t nqt = (N + kBwdBlockM - 1) / kBwdBlockM;
+  const int64_t G = H_q / H_kv_local;
+  int64_t nnz = 0;
+  cowa_status st = plan_size_memo(p, N, H_kv_local, kBwdBlockM, kBwdBlockN, &nnz);
+  if (st != COWA_OK) return st;
+  const int64_t mean_steps = (G * nnz + (int64_t)H_kv_local * nkt - 1) / ((int64_t)H_kv_local * nkt);
+  const int64_t cap = mean_steps * 2 > 256 ? mean_steps * 2 : 256;
+  const int64_t nch = (G * nqt + cap - 1) / cap;
+  const int32_t sink_tiles = (int32_t)(((int64_t)p->sink + kBwdBlockN - 1) / kBwdBlockN);
+  g->n_sink_tiles = nch > 1 ? (sink_tiles < nkt ? sink_tiles : nkt) : 0;
+  g->nch = g->n_sink_tiles > 0 ? (int32_t)nch : 1;
+  const size_t part_bytes = (size_t)B * H_kv_local * g->n_sink_tiles * g->nch * 2 * kBwdBlockN *
+                            128 * sizeof(float);
+  g->total_bytes = g->part_offset + part_bytes;
+  return COWA_OK;
 }
 }  // namespace
 
-extern "C" cowa_status cowa_bwd_workspace_size(int32_t B, int32_t H_q, int32_t N, size_t* bytes) {
-  if (!bytes || B < 1 || H_q < 1 || N < 1) return COWA_ERR_INVALID_ARG;
-  *bytes = bwd_geometry(B, H_q, N).total_bytes;
+extern "C" cowa_status cowa_bwd_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,
+                                               int32_t H_kv_local, int32_t N, size_t* bytes) {
+  cowa_status st = validate_pattern(p, H_kv_local);
+  if (st != COWA_OK) return st;
+  if (!bytes || B < 1 || H_q < 1 || N < 1 || H_q % H_kv_local != 0) return COWA_ERR_INVALID_ARG;
+  BwdGeometry g;
+  st = bwd_geometry(p, B, H_q, H_kv_local, N, &g);
+  if (st != COWA_OK) return st;
+  *bytes = g.total_bytes;
   return COWA_OK;
 }
 
@@ -300,9 +326,14 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   st = plan_size_memo(p, N, H_kv_local, block_m_kv, block_n_kv, &want);
   if (st != COWA_OK) return st;
   if (want != nnz_kv) return COWA_ERR_PLAN_MISMATCH;
-  const BwdGeometry geo = bwd_geometry(B, H_q, N);
+  BwdGeometry geo;
+  st = bwd_geometry(p, B, H_q, H_kv_local, N, &geo);
+  if (st != COWA_OK) return st;
   if (!workspace || ws_bytes < geo.total_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return COWA_ERR_WORKSPACE;
+  if ((int64_t)B * H_kv_local * (nkt_kv + (int64_t)geo.n_sink_tiles * (geo.nch - 1)) >
+      0x7fffffffLL)
+    return COWA_ERR_UNSUPPORTED;
 
   BwdParams bp;
   bp.row_ptr = d_row_ptr;
@@ -322,6 +353,9 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   bp.dv = dv;
   bp.lse2 = static_cast<float*>(workspace);
   bp.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.delta_offset);
+  bp.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.part_offset);
+  bp.n_sink_tiles = geo.n_sink_tiles;
+  bp.nch = geo.nch;
   int64_t* const dst[24] = {&bp.qs_b,  &bp.qs_t,  &bp.qs_h,  &bp.ks_b,  &bp.ks_t,  &bp.ks_h,
                             &bp.vs_b,  &bp.vs_t,  &bp.vs_h,  &bp.os_b,  &bp.os_t,  &bp.os_h,
                             &bp.dos_b, &bp.dos_t, &bp.dos_h, &bp.dqs_b, &bp.dqs_t, &bp.dqs_h,

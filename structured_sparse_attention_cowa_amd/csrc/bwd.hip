@@ -25,7 +25,10 @@
 //          64-row query tile: S = Q K^T, dP = dO V^T (lane = key column), then
 //          dV^T += dO^T P and dK^T += Q^T dS with dO and Q read transposed.
 //          Summing the group's query heads inside the workgroup needs no
-//          atomics, and the result is deterministic.
+//          atomics.  Key tiles holding sink keys are seen by every query
+//          tile; their step lists are cut into parts that run as separate
+//          workgroups writing fp32 partials, which a last kernel sums in a
+//          fixed order, so the result stays deterministic.
 // Tiles stream from HBM straight into LDS (16 bytes per lane), double
 // buffered, with one swizzle that serves both the plain and the transposing
 // reads without bank conflicts.
@@ -96,8 +99,9 @@ __device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][NK]
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      const int row = 32 * blk + l32;
-      off[blk][ks] = row * D + (((2 * ks + hl) ^ swz_both_d128(row)) * 8);
+      // rows l32 and 32 + l32 share the swizzle: the two blocks differ by a
+      // constant, which the compiler folds into the read's offset field
+      off[blk][ks] = 32 * blk * D + l32 * D + (((2 * ks + hl) ^ swz_both_d128(l32)) * 8);
     }
 }
 
@@ -117,6 +121,45 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][ND]) {
     }
 }
 
+// An empty use of loaded registers: the loads must have completed here, so
+// the tile loops that follow start with no register load in flight.
+template <int N>
+__device__ __forceinline__ void complete(const bf16x8 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : : "v"(r[i]));
+}
+
+// Plan entries (tile index, full-tile flag in bit 31) travel 64 at a time,
+// one per lane, and are picked out with readlane.  A plain per-step load
+// would have to complete before the tile loads that follow it in the same
+// step can be left in flight.
+struct PlanCursor {
+  const int32_t* col;
+  const uint8_t* flags;
+  int end;
+  int base;
+  int chunk;
+  __device__ int fetch(int b0, int lane) const {
+    const int e = b0 + lane;
+    return e < end ? (col[e] | (flags[e] ? (int)0x80000000 : 0)) : 0;
+  }
+  __device__ void init(const int32_t* c, const uint8_t* f, int e_begin, int e_end, int lane) {
+    col = c;
+    flags = f;
+    end = e_end;
+    base = e_begin;
+    chunk = fetch(base, lane);
+  }
+  // entry e (wave-uniform); reloads the chunk when e leaves it
+  __device__ int entry(int e, int lane) {
+    if (e < base || e >= base + 64) {
+      base = e;
+      chunk = fetch(base, lane);
+    }
+    return __builtin_amdgcn_readlane(chunk, e - base);
+  }
+};
+
 // ------------------------------------------------------------------- dQ --
 constexpr int QBM = kFwdBlockM;  // 256 query rows per workgroup
 constexpr int QBN = kFwdBlockN;  // 64 keys per tile
@@ -129,9 +172,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   constexpr int TILE = QBN * D;
   constexpr int LOADS = QBN * CPR / 64 / QWAVES;
   static_assert(LOADS >= 1, "every wavefront loads part of each tile");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K[2], V[2]
-  uint16_t* const Kbuf = smem;
-  uint16_t* const Vbuf = smem + 2 * TILE;
+  // One LDS variable per buffer: the compiler tells distinct variables apart,
+  // so the loads streaming into one buffer stay in flight while the step
+  // reads the other (within one variable it would wait for them first).
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,21 +223,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
 
-  int ld_row[LOADS], ld_col[LOADS], ld_koff[LOADS], ld_voff[LOADS];
+  // lane offsets inside a tile are unsigned 32-bit (the host bounds 64 rows x
+  // stride below 2^31), so the loads use a uniform 64-bit base plus a 32-bit offset
+  int ld_row[LOADS], ld_col[LOADS];
+  uint32_t ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
     ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
-    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_col[i];
-    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_col[i];
+    ld_koff[i] = (uint32_t)(ld_row[i] * p.ks_t) + ld_col[i];
+    ld_voff[i] = (uint32_t)(ld_row[i] * p.vs_t) + ld_col[i];
   }
   // K and V tiles of key tile kj into buffer slot; keys past N (only in
   // tiles the plan marks partial, where they are masked) are clamped.
-  auto load_kv = [&](int kj, int slot) {
+  auto load_kv = [&](int kj, uint16_t* kd, uint16_t* vd) {
     const int key0 = kj * QBN;
-    uint16_t* kd = Kbuf + slot * TILE;
-    uint16_t* vd = Vbuf + slot * TILE;
     if (key0 + QBN <= p.N) {
       const uint16_t* kt = kbase + (int64_t)key0 * p.ks_t;
       const uint16_t* vt = vbase + (int64_t)key0 * p.vs_t;
@@ -214,30 +262,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   plain_offsets(l32, hl, n_off);
   tr_offsets(lane, t_off);
 
-  auto entry = [&](int e) { return p.col[e] | (p.flags[e] ? (int)0x80000000 : 0); };
+  PlanCursor pc;
+  pc.init(p.col, p.flags, e0, e1, lane);
+  // The register operands and the first plan chunk are complete on every path
+  // into the tile loop (otherwise the loop waits for its own prefetch).
+  complete(qf);
+  complete(dof);
+  asm volatile("" : : "v"(lse2), "v"(dlt), "v"(pc.chunk));
 
   int c_cur = 0;
   if (e0 < e1) {
-    c_cur = entry(e0);
-    load_kv(c_cur & 0x7fffffff, 0);
+    c_cur = pc.entry(e0, lane);
+    load_kv(c_cur & 0x7fffffff, K0, V0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int e = e0; e < e1; ++e) {
-    const int slot = (e - e0) & 1;
+  // One step on the tiles in (Ks, Vs) while the next ones stream into (Kn, Vn).
+  auto step = [&](int e, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
     int c_nxt = 0;
     if (e + 1 < e1) {
-      c_nxt = entry(e + 1);
-      load_kv(c_nxt & 0x7fffffff, slot ^ 1);
+      c_nxt = pc.entry(e + 1, lane);
+      load_kv(c_nxt & 0x7fffffff, Kn, Vn);
     }
     const int kj = c_cur & 0x7fffffff;
     const bool full = c_cur < 0;
-    const uint16_t* Ks = Kbuf + slot * TILE;
-    const uint16_t* Vs = Vbuf + slot * TILE;
 
-    unsigned pk[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      unsigned pk[8];
       f32x16 s = f32x16{}, dpv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
@@ -268,24 +320,29 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], p.scale_log2, -lse2));
         const float p1 =
             __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], p.scale_log2, -lse2));
-        pk[blk][i] = pack_bf16(p0 * (dpv[2 * i] - dlt), p1 * (dpv[2 * i + 1] - dlt));
+        pk[i] = pack_bf16(p0 * (dpv[2 * i] - dlt), p1 * (dpv[2 * i + 1] - dlt));
       }
-    }
+      // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int blk = st >> 1, o4 = (st & 1) * 4;
-      const u32x4 w = {pk[blk][o4], pk[blk][o4 + 1], pk[blk][o4 + 2], pk[blk][o4 + 3]};
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, w);
+      for (int half = 0; half < 2; ++half) {
+        const int st = 2 * blk + half, o4 = half * 4;
+        const u32x4 w = {pk[o4], pk[o4 + 1], pk[o4 + 2], pk[o4 + 3]};
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 a =
-            lds_read_tr_pair(Ks + st * 16 * D + t_off[0][db], Ks + st * 16 * D + t_off[1][db]);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 a =
+              lds_read_tr_pair(Ks + st * 16 * D + t_off[0][db], Ks + st * 16 * D + t_off[1][db]);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
+        }
       }
     }
     c_cur = c_nxt;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int e = e0; e < e1; e += 2) {
+    step(e, K0, V0, K1, V1);
+    if (e + 1 < e1) step(e + 1, K1, V1, K0, V0);
   }
 
   if (q_row < p.N) {
@@ -338,10 +395,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   constexpr int TILE = KBM * D;
   constexpr int LOADS = KBM * CPR / 64 / KWAVES;
   static_assert(LOADS >= 1, "every wavefront loads part of each tile");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // Q[2], dO[2]
-  __shared__ __attribute__((aligned(16))) float stats[2][2][KBM];   // [slot][LSE2, D][row]
-  uint16_t* const Qbuf = smem;
-  uint16_t* const Obuf = smem + 2 * TILE;
+  // one LDS variable per buffer (as in the dQ kernel); S0, S1 hold LSE2 then D
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[TILE];
+  __shared__ __attribute__((aligned(16))) float S0[2 * KBM];
+  __shared__ __attribute__((aligned(16))) float S1[2 * KBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -349,14 +409,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
-  // key tiles in ascending order: the early ones (sink, and in causal mode
-  // the longest columns) carry the most query tiles
-  const int per_kj = p.B * p.Hkv;
-  const int wg = blockIdx.x;
-  const int kj = wg / per_kj;
-  const int rem = wg - kj * per_kj;
-  const int b = rem / p.Hkv;
-  const int h = rem - b * p.Hkv;
+  // First the parts of the split sink key tiles, then the other key tiles in
+  // ascending order (in causal mode the early ones carry the most query tiles).
+  const int n_part_wg = p.B * p.Hkv * p.n_sink_tiles * p.nch;
+  int wg = blockIdx.x;
+  int b, h, kj, part = -1;
+  if (wg < n_part_wg) {
+    part = wg % p.nch;
+    int t = wg / p.nch;
+    kj = t % p.n_sink_tiles;
+    t /= p.n_sink_tiles;
+    h = t % p.Hkv;
+    b = t / p.Hkv;
+  } else {
+    wg -= n_part_wg;
+    const int per_kj = p.B * p.Hkv;
+    kj = p.n_sink_tiles + wg / per_kj;
+    const int rem = wg % per_kj;
+    b = rem / p.Hkv;
+    h = rem - b * p.Hkv;
+  }
   const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
 
   const int key = kj * KBN + wave * 32 + l32;
@@ -378,28 +450,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     dv[i] = f32x16{};
   }
 
+  // steps run over (query head of the group, visible query tile); a part
+  // takes one contiguous range of them
   const int r = h * p.nkt_kv + kj;
   const int e0 = p.row_ptr_kv[r];
   const int e1 = p.row_ptr_kv[r + 1];
-  const int nsteps = (e1 - e0) * p.G;
+  const int cnt = e1 - e0;
+  const int total = cnt * p.G;
+  int s_begin = 0, s_end = total;
+  if (part >= 0) {
+    const int len = (total + p.nch - 1) / p.nch;
+    s_begin = min(total, part * len);
+    s_end = min(total, s_begin + len);
+  }
+  const int nsteps = s_end - s_begin;
 
-  int ld_row[LOADS], ld_col[LOADS], ld_qoff[LOADS], ld_ooff[LOADS];
+  int ld_row[LOADS], ld_col[LOADS];
+  uint32_t ld_qoff[LOADS], ld_ooff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
     ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
-    ld_qoff[i] = (int)(ld_row[i] * p.qs_t) + ld_col[i];
-    ld_ooff[i] = (int)(ld_row[i] * p.dos_t) + ld_col[i];
+    ld_qoff[i] = (uint32_t)(ld_row[i] * p.qs_t) + ld_col[i];
+    ld_ooff[i] = (uint32_t)(ld_row[i] * p.dos_t) + ld_col[i];
   }
   // Q and dO rows of query tile qi of head hq into buffer slot, with that
   // tile's LSE2 and D; rows past N are clamped (their LSE2 is +inf).
-  auto load_q = [&](int hq, int qi, int slot) {
+  auto load_q = [&](int hq, int qi, uint16_t* qd, uint16_t* od, float* sdst) {
     const int r0 = qi * KBM;
     const uint16_t* qb = p.q + (int64_t)b * p.qs_b + (int64_t)hq * p.qs_h;
     const uint16_t* ob = p.dout + (int64_t)b * p.dos_b + (int64_t)hq * p.dos_h;
-    uint16_t* qd = Qbuf + slot * TILE;
-    uint16_t* od = Obuf + slot * TILE;
     if (r0 + KBM <= p.N) {
       const uint16_t* qt = qb + (int64_t)r0 * p.qs_t;
       const uint16_t* ot = ob + (int64_t)r0 * p.dos_t;
@@ -418,47 +499,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
       }
     }
     const int64_t so = ((int64_t)b * p.Hq + hq) * p.npad + r0;
-    if (wave == 0) g2lds4(p.lse2 + so + lane, &stats[slot][0][0]);
-    if (wave == 1) g2lds4(p.delta + so + lane, &stats[slot][1][0]);
+    if (wave == 0) g2lds4(p.lse2 + so + lane, sdst);
+    if (wave == 1) g2lds4(p.delta + so + lane, sdst + KBM);
   };
 
   int n_off[2][NK], t_off[2][ND];
   plain_offsets(l32, hl, n_off);
   tr_offsets(lane, t_off);
 
-  auto entry = [&](int e) { return p.col_kv[e] | (p.flags_kv[e] ? (int)0x80000000 : 0); };
-
-  // steps run over (query head of the group, visible query tile)
   int hq_cur = h * p.G, e_cur = e0, c_cur = 0;
+  if (cnt > 0) {
+    hq_cur += s_begin / cnt;
+    e_cur += s_begin % cnt;
+  }
+  PlanCursor pc;
+  pc.init(p.col_kv, p.flags_kv, e_cur, e1, lane);
+  // K, V registers and the first plan chunk complete on every path into the loop
+  complete(kf);
+  complete(vf);
+  asm volatile("" : : "v"(pc.chunk));
   if (nsteps > 0) {
-    c_cur = entry(e0);
-    load_q(hq_cur, c_cur & 0x7fffffff, 0);
+    c_cur = pc.entry(e_cur, lane);
+    load_q(hq_cur, c_cur & 0x7fffffff, Q0, O0, S0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
   const bool key_sink = key < hp.sink;
-  for (int s = 0; s < nsteps; ++s) {
-    const int slot = s & 1;
+  // One step on the tiles in (Qs, Os, Ss) while the next ones stream into
+  // (Qn, On, Sn).
+  auto step = [&](int s, const uint16_t* Qs, const uint16_t* Os, const float* Ss, uint16_t* Qn,
+                  uint16_t* On, float* Sn) {
+    const float* sl = Ss;
+    const float* sd = Ss + KBM;
     int hq_nxt = hq_cur, e_nxt = e_cur + 1, c_nxt = 0;
     if (e_nxt == e1) {
       e_nxt = e0;
       ++hq_nxt;
     }
     if (s + 1 < nsteps) {
-      c_nxt = entry(e_nxt);
-      load_q(hq_nxt, c_nxt & 0x7fffffff, slot ^ 1);
+      c_nxt = pc.entry(e_nxt, lane);
+      load_q(hq_nxt, c_nxt & 0x7fffffff, Qn, On, Sn);
     }
     const int qi = c_cur & 0x7fffffff;
     const bool full = c_cur < 0;
-    const uint16_t* Qs = Qbuf + slot * TILE;
-    const uint16_t* Os = Obuf + slot * TILE;
-    const float* sl = stats[slot][0];
-    const float* sd = stats[slot][1];
 
-    unsigned pp[2][8], ps[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      unsigned pp[8], ps[8];
       f32x16 sv = f32x16{}, dpv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
@@ -491,30 +579,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
           pv[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * j + u], p.scale_log2, -l4[u]));
           dsv[u] = pv[u] * (dpv[4 * j + u] - d4[u]);
         }
-        pp[blk][2 * j] = pack_bf16(pv[0], pv[1]);
-        pp[blk][2 * j + 1] = pack_bf16(pv[2], pv[3]);
-        ps[blk][2 * j] = pack_bf16(dsv[0], dsv[1]);
-        ps[blk][2 * j + 1] = pack_bf16(dsv[2], dsv[3]);
+        pp[2 * j] = pack_bf16(pv[0], pv[1]);
+        pp[2 * j + 1] = pack_bf16(pv[2], pv[3]);
+        ps[2 * j] = pack_bf16(dsv[0], dsv[1]);
+        ps[2 * j + 1] = pack_bf16(dsv[2], dsv[3]);
       }
-    }
+      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 query rows
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int blk = st >> 1, o4 = (st & 1) * 4;
-      const u32x4 wp = {pp[blk][o4], pp[blk][o4 + 1], pp[blk][o4 + 2], pp[blk][o4 + 3]};
-      const u32x4 ws = {ps[blk][o4], ps[blk][o4 + 1], ps[blk][o4 + 2], ps[blk][o4 + 3]};
-      const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
-      const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
+      for (int half = 0; half < 2; ++half) {
+        const int st = 2 * blk + half, o4 = half * 4;
+        const u32x4 wp = {pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]};
+        const u32x4 ws = {ps[o4], ps[o4 + 1], ps[o4 + 2], ps[o4 + 3]};
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
+        const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 a =
-            lds_read_tr_pair(Os + st * 16 * D + t_off[0][db], Os + st * 16 * D + t_off[1][db]);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, dv[db], 0, 0, 0);
-      }
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 a = lds_read_tr_pair(Os + st * 16 * D + t_off[0][db],
+                                            Os + st * 16 * D + t_off[1][db]);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, dv[db], 0, 0, 0);
+        }
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 a =
-            lds_read_tr_pair(Qs + st * 16 * D + t_off[0][db], Qs + st * 16 * D + t_off[1][db]);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, dk[db], 0, 0, 0);
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 a = lds_read_tr_pair(Qs + st * 16 * D + t_off[0][db],
+                                            Qs + st * 16 * D + t_off[1][db]);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, dk[db], 0, 0, 0);
+        }
       }
     }
     hq_cur = hq_nxt;
@@ -522,15 +611,66 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     c_cur = c_nxt;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int s = 0; s < nsteps; ++s) {
+    if (s & 1)
+      step(s, Q1, O1, S1, Q0, O0, S0);
+    else
+      step(s, Q0, O0, S0, Q1, O1, S1);
   }
 
-  if (key < p.N) {
+  if (part >= 0) {
+    // fp32 partials [b][h][sink tile][part][dK, dV][key][d]
+    const int64_t slot =
+        (((int64_t)(b * p.Hkv + h) * p.n_sink_tiles + kj) * p.nch + part) * 2;
+    const int64_t row = (int64_t)(wave * 32 + l32) * D;
+    store_key_row<true>(p.part, slot * KBN * D + row, dk, p.scale, hl);
+    store_key_row<true>(p.part, (slot + 1) * KBN * D + row, dv, 1.f, hl);
+  } else if (key < p.N) {
     store_key_row<GF32>(p.dk,
                         (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h, dk,
                         p.scale, hl);
     store_key_row<GF32>(p.dv,
                         (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h, dv,
                         1.f, hl);
+  }
+}
+
+// Sum of the parts of the split sink key tiles, in part order.  Grid
+// (H_kv * n_sink_tiles, B); each thread covers 8 head dims of 8 keys.
+template <bool GF32>
+__global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) {
+  const int t = blockIdx.x;
+  const int kj = t % p.n_sink_tiles;
+  const int h = t / p.n_sink_tiles;
+  const int b = blockIdx.y;
+  const int64_t slot0 = (((int64_t)(b * p.Hkv + h) * p.n_sink_tiles + kj) * p.nch) * 2;
+  for (int u = threadIdx.x; u < KBN * (D / 8); u += 256) {
+    const int kl = u / (D / 8);
+    const int d0 = (u % (D / 8)) * 8;
+    const int key = kj * KBN + kl;
+    if (key >= p.N) continue;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      f32x4 a = {}, c = {};
+      for (int part = 0; part < p.nch; ++part) {
+        const float* src = p.part + ((slot0 + 2 * part + which) * KBN + kl) * D + d0;
+        a += *reinterpret_cast<const f32x4*>(src);
+        c += *reinterpret_cast<const f32x4*>(src + 4);
+      }
+      void* dst = which == 0 ? p.dk : p.dv;
+      const int64_t idx = which == 0
+          ? (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h + d0
+          : (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h + d0;
+      if (GF32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + idx) = a;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + idx + 4) = c;
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + idx) =
+            u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c[0], c[1]),
+                  pack_bf16(c[2], c[3])};
+      }
+    }
   }
 }
 
@@ -542,13 +682,19 @@ int launch_bwd(const BwdParams& p, int d, void* stream) {
   hipLaunchKernelGGL(cowa_bwd_delta_kernel, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
                      dim3(256), 0, s, p);
   const dim3 gq((unsigned)((int64_t)p.B * p.nqt * p.Hq));
-  const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.nkt_kv));
+  const dim3 gk((unsigned)((int64_t)p.B * p.Hkv *
+                           (p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1))));
+  const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles), (unsigned)p.B);
   if (p.g_f32) {
     hipLaunchKernelGGL(cowa_bwd_dq_kernel<true>, gq, dim3(QTHREADS), 0, s, p);
     hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<true>, gk, dim3(KTHREADS), 0, s, p);
+    if (p.n_sink_tiles > 0)
+      hipLaunchKernelGGL(cowa_bwd_part_reduce_kernel<true>, gr, dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL(cowa_bwd_dq_kernel<false>, gq, dim3(QTHREADS), 0, s, p);
     hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<false>, gk, dim3(KTHREADS), 0, s, p);
+    if (p.n_sink_tiles > 0)
+      hipLaunchKernelGGL(cowa_bwd_part_reduce_kernel<false>, gr, dim3(256), 0, s, p);
   }
   return (int)hipGetLastError();
 }

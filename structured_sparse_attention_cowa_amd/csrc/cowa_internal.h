@@ -113,7 +113,10 @@ struct BwdParams {
   int64_t dqs_b, dqs_t, dqs_h;
   int64_t dks_b, dks_t, dks_h;
   int64_t dvs_b, dvs_t, dvs_h;
+  float* part;   // workspace: fp32 dK, dV partials of the split sink key tiles
   int32_t B, N, Hq, Hkv, G, nqt, nkt_kv, nqt_kv, npad;
+  int32_t n_sink_tiles;  // leading key tiles whose step lists are split (0: none)
+  int32_t nch;           // parts per split key tile
   int32_t sink, window, band, kv_head_offset, causal;
   int32_t o_f32, g_f32;
   float scale;

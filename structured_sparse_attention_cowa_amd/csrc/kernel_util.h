@@ -86,10 +86,11 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint16_t* lo, const uin
 // by this function of the row are free of bank conflicts both for 16-byte
 // reads of one chunk column by 16 consecutive rows and for transposing reads
 // of 4 consecutive rows x 2-4 adjacent chunks.
+// The value is [0, 6, 12, 10][row % 4] ^ ((row / 4) % 4), written with bit
+// operations so that the compiler can bound it (and the offsets built from it).
 __device__ __forceinline__ int swz_both_d128(int row) {
   const int a = row & 3;
-  const int base = a == 0 ? 0 : (a == 1 ? 6 : (a == 2 ? 12 : 10));
-  return base ^ ((row >> 2) & 3);
+  return (((a << 2) ^ (a << 1)) & 14) ^ ((row >> 2) & 3);
 }
 
 }  // namespace kern

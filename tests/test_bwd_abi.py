@@ -68,11 +68,26 @@ def test_bwd_block_sizes_and_workspace(lib):
     with pytest.raises(C.CowaError) as e:
         C.cowa_bwd_block_sizes(64)
     assert e.value.status == C.COWA_ERR_UNSUPPORTED
-    # two fp32 arrays [B, H_q, N rounded up to 64], each 256-byte aligned
-    assert C.cowa_bwd_workspace_size(1, 1, 1) == 2 * 256
-    assert C.cowa_bwd_workspace_size(2, 5, 130) == 2 * (2 * 5 * 192 * 4)
+    # two fp32 arrays [B, H_q, N rounded up to 64], each 256-byte aligned, when
+    # no key tile's step list is split
+    cp, _ = pat(n_ctx=130, sink=0, window=16, h_kv_global=1)
+    assert C.cowa_bwd_workspace_size(cp, 1, 1, 1, 1) == 2 * 256
+    assert C.cowa_bwd_workspace_size(cp, 2, 5, 1, 130) == 2 * (2 * 5 * 192 * 4)
     with pytest.raises(C.CowaError):
-        C.cowa_bwd_workspace_size(0, 1, 1)
+        C.cowa_bwd_workspace_size(cp, 0, 1, 1, 1)
+    with pytest.raises(C.CowaError):
+        C.cowa_bwd_workspace_size(cp, 1, 3, 2, 1)
+    # 128K rank: the sink key tile (seen by all 2048 query tiles x 5 heads) is
+    # cut into parts; their fp32 dK/dV partials follow LSE2 and D
+    w = W.P128K
+    cp, _ = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8)
+    base = 2 * (5 * w.N * 4)
+    ws = C.cowa_bwd_workspace_size(cp, 1, 5, 1, w.N)
+    part = 2 * 128 * 128 * 4
+    assert ws > base and (ws - base) % part == 0 and (ws - base) // part >= 2
+    # causal mode: no key tile exceeds twice the mean, nothing is split
+    cpc, _ = pat(n_ctx=w.N, sink=w.sink, window=w.window, h_kv_global=8, mode=1)
+    assert C.cowa_bwd_workspace_size(cpc, 1, 5, 1, w.N) == base
 
 
 def _bwd_raw(lib, cp, N=256, Hq=4, Hkv=2, d=128, B=1, nnz=None, nnz_kv=None, bm=None, bn=None,
@@ -94,8 +109,8 @@ def _bwd_raw(lib, cp, N=256, Hq=4, Hkv=2, d=128, B=1, nnz=None, nnz_kv=None, bm=
         nnz = C.cowa_plan_size(cp, N, Hkv, fbm, fbn)
     if nnz_kv is None:
         nnz_kv = C.cowa_plan_kv_size(cp, N, Hkv, kbm, kbn)
-    if ws_bytes is None:
-        ws_bytes = C.cowa_bwd_workspace_size(B, Hq, N)
+    if ws_bytes is None:  # large enough for any case here (shapes are rejected first)
+        ws_bytes = 1 << 30
     arr = (ctypes.c_int64 * 24)(*(strides if strides is not None else [8] * 24))
     P = ptrs
     return lib.cowa_bwd(ctypes.byref(cp), P["rp"], P["col"], P["fl"], nnz, bm, bn, P["rpk"],
@@ -122,7 +137,7 @@ def test_bwd_host_validation(lib):
     for nm in ("rp", "col", "fl", "rpk", "colk", "flk", "q", "k", "v", "o", "do", "lse", "dq",
                "dk", "dv"):
         assert _bwd_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
-    ws = C.cowa_bwd_workspace_size(1, 4, 256)
+    ws = C.cowa_bwd_workspace_size(cp, 1, 4, 2, 256)
     assert _bwd_raw(lib, cp, ws_bytes=ws - 1) == E.COWA_ERR_WORKSPACE
     assert _bwd_raw(lib, cp, ws_ptr=0) == E.COWA_ERR_WORKSPACE
     assert _bwd_raw(lib, cp, ws_ptr=0x100040) == E.COWA_ERR_WORKSPACE
