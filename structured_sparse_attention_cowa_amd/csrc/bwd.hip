@@ -637,19 +637,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
 }
 
 // Sum of the parts of the split sink key tiles, in part order.  Grid
-// (H_kv * n_sink_tiles, B); each thread covers 8 head dims of 8 keys.
+// (H_kv * n_sink_tiles * REDUCE_SPLIT, B); each workgroup covers 16 keys,
+// each thread 8 head dims of one key.
+constexpr int REDUCE_SPLIT = KBN / 16;
 template <bool GF32>
 __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) {
-  const int t = blockIdx.x;
+  const int t = blockIdx.x / REDUCE_SPLIT;
   const int kj = t % p.n_sink_tiles;
   const int h = t / p.n_sink_tiles;
   const int b = blockIdx.y;
   const int64_t slot0 = (((int64_t)(b * p.Hkv + h) * p.n_sink_tiles + kj) * p.nch) * 2;
-  for (int u = threadIdx.x; u < KBN * (D / 8); u += 256) {
+  {
+    const int u = (blockIdx.x % REDUCE_SPLIT) * 256 + threadIdx.x;  // 16 keys x 16 chunks
     const int kl = u / (D / 8);
     const int d0 = (u % (D / 8)) * 8;
     const int key = kj * KBN + kl;
-    if (key >= p.N) continue;
+    if (key >= p.N) return;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       f32x4 a = {}, c = {};
@@ -684,7 +687,7 @@ int launch_bwd(const BwdParams& p, int d, void* stream) {
   const dim3 gq((unsigned)((int64_t)p.B * p.nqt * p.Hq));
   const dim3 gk((unsigned)((int64_t)p.B * p.Hkv *
                            (p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1))));
-  const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles), (unsigned)p.B);
+  const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles * REDUCE_SPLIT), (unsigned)p.B);
   if (p.g_f32) {
     hipLaunchKernelGGL(cowa_bwd_dq_kernel<true>, gq, dim3(QTHREADS), 0, s, p);
     hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<true>, gk, dim3(KTHREADS), 0, s, p);

@@ -75,10 +75,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
   constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
 
-  // K tiles [2] then V tiles [2]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
-  uint16_t* const Kbuf = smem;
-  uint16_t* const Vbuf = smem + 2 * TILE;
+  // One LDS variable per tile buffer: the compiler tells distinct variables
+  // apart, so the loads streaming into one buffer stay in flight while the
+  // step reads another (within one variable it would wait for them first).
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,6 +108,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks + 8 * hl));
+    // complete before the tile loop, which then starts with no register load
+    // in flight (otherwise it waits for its own prefetch)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) asm volatile("" : : "v"(qf[ks]));
   }
 
   f32x16 acc[ND];
@@ -208,19 +215,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   if (e0 < e1) {
     c_cur = entry(e0);
     c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
-    load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_cur & 0x7fffffff, Kbuf);
-    load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_cur & 0x7fffffff, Vbuf);
-    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n1 & 0x7fffffff, Kbuf + TILE);
+    load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_cur & 0x7fffffff, K0);
+    load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_cur & 0x7fffffff, V0);
+    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n1 & 0x7fffffff, K1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    qk(Kbuf, s_first);
+    qk(K0, s_first);
     // every wave has read K(e0) before its buffer is refilled
     __syncthreads();
   }
 
-  // one pipeline step for tile e; s_cur holds S(e), s_nxt receives S(e+1)
-  auto step = [&](int e, f32x16* s_cur, f32x16* s_nxt) {
-    const int slot = (e - e0) & 1;
+  // One pipeline step for tile e; s_cur holds S(e), s_nxt receives S(e+1).
+  // Reads K(e+1) from Kr and V(e) from Vr; K(e+2) streams into Kw, V(e+1) into Vw.
+  auto step = [&](int e, f32x16* s_cur, f32x16* s_nxt, const uint16_t* Kr, const uint16_t* Vr,
+                  uint16_t* Kw, uint16_t* Vw) {
     const int kj = c_cur & 0x7fffffff;
     const bool full = c_cur < 0;
     const bool has_next = e + 1 < e1;
@@ -232,9 +240,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pchunk = plan_chunk(pbase);
       }
       c_n2 = entry(e + 2);
-      load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n2 & 0x7fffffff, Kbuf + slot * TILE);
+      load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n2 & 0x7fffffff, Kw);
     }
-    if (has_next) load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_n1 & 0x7fffffff, Vbuf + (slot ^ 1) * TILE);
+    if (has_next) load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_n1 & 0x7fffffff, Vw);
 
     if (!full) {
       // branch-free form of the visibility predicate vis_g(t, j)
@@ -276,7 +284,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     // ---- one basic block: S(e+1) MFMAs, softmax of S(e), P.V MFMAs ----
     // (unconditional so that the scheduler can interleave it with the
     // softmax; on a row's last tile it reads a stale buffer and is unused)
-    qk(Kbuf + (slot ^ 1) * TILE, s_nxt);
+    qk(Kr, s_nxt);
     unsigned pk[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -287,7 +295,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pk[blk][i] = pack_bf16(a, c);
         l_run += a + c;
       }
-    const uint16_t* Vs = Vbuf + slot * TILE;
+    const uint16_t* Vs = Vr;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int blk = st >> 1;
@@ -329,11 +337,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  // unrolled by two so the two S register sets alternate without copies
+  // unrolled by two so the two S register sets and the buffers alternate
+  // without copies or run-time buffer selection
   f32x16 s_alt[2];
   for (int e = e0; e < e1; e += 2) {
-    step(e, s_first, s_alt);
-    if (e + 1 < e1) step(e + 1, s_alt, s_first);
+    step(e, s_first, s_alt, K1, V0, K0, V1);
+    if (e + 1 < e1) step(e + 1, s_alt, s_first, K0, V1, K1, V0);
   }
 
   const float l_tot = pair_sum(l_run);
