@@ -246,7 +246,20 @@ def main():
                                                         wd.n_max), dtype=torch.uint8, device=dev)
         dec_causal_ms = time_it(lambda: C.cowa_decode(pd_c, qd, kc, vc, sl, od, lsed,
                                                       1.0 / np.sqrt(wd.d), ws_c), 3)
+        # pattern variants on the same kernels: sliding-window attention with
+        # sinks (no band) at the 128K rank, and the 8K ablation setting (8 KV
+        # heads) with 1, 2, 4, 8 distinct long-range windows
+        sl_plan = make_plan(0, mode=2)
+        sl_ms = time_it(lambda: prefill(sl_plan), 3)
+        sl_pairs = int(visible_counts(t_all, 0, wp.sink, wp.window, 0).sum())
+        sl_flops = 4.0 * d * G * B * sl_pairs
+        variants = {"sink_local_128k": {"ms": round(sl_ms, 4),
+                                        "tflops": round(sl_flops / (sl_ms * 1e-3) / 1e12, 1),
+                                        "mfma_frac": round(sl_flops / (sl_ms * 1e-3) / 1e12
+                                                           / PEAK_BF16_TFLOPS, 4)},
+                    "ablation_8k": ablation_8k(C, W, torch, dev, to_dev, time_it)}
         extras = {
+            "variants": variants,
             "prefill_per_g": [{"g": g, "ms": round(per_g[g], 4),
                                "tflops": round(flops[g] / (per_g[g] * 1e-3) / 1e12, 1),
                                "mfma_frac": round(flops[g] / (per_g[g] * 1e-3) / 1e12
@@ -334,6 +347,32 @@ def main():
     }
     out.update(extras)
     print(json.dumps(out), flush=True)
+
+
+def ablation_8k(C, W, torch, dev, to_dev, time_it):
+    """Prefill of the 8K workload (B=2, N=8192, H_q=32, H_kv=8, S=64, W=1024,
+    L=896) with m distinct long-range windows shared out over the 8 KV heads."""
+    w = W.P8K
+    x = W.prefill_inputs(w)
+    q, k, v = to_dev(x.q_bits), to_dev(x.k_bits), to_dev(x.v_bits)
+    o = torch.empty((w.B, w.N, w.H_q, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+    bm, bn = C.cowa_fwd_block_sizes(w.d)
+    G = w.H_q // w.H_kv
+    t = np.arange(w.N)
+    out = []
+    for m in (1, 2, 4, 8):
+        p = C.make_pattern(w.N, w.sink, w.window, 0, w.h_kv_global, 0, 0, m)
+        rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, w.N, w.H_kv, bm, bn)]
+        ms = time_it(lambda: C.cowa_fwd(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
+                                        1.0 / np.sqrt(w.d)), 5)
+        pairs = sum(int(visible_counts(t, g % m, w.sink, w.window, w.stated_band).sum())
+                    for g in range(w.H_kv))
+        flops = 4.0 * w.d * G * w.B * pairs
+        out.append({"distinct_windows": m, "ms": round(ms, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    return out
 
 
 def cpu_baseline(x, wp, scale, target_s=12.0):

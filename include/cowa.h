@@ -22,6 +22,15 @@
  * g = kv_head_offset + h.  In COWA_MODE_CAUSAL, vis(t, j) = j <= t (the dense
  * FullAttn comparison, Abstract).
  *
+ * Pattern variants on the same kernels:
+ *  - n_bands = m < h_kv_global: the duplicated-window ablation of the news
+ *    page (ablation paragraph: 1, 2, 4, 8 distinct long-range windows over 8
+ *    KV heads at fixed per-head width).  Head g takes window b = g mod m,
+ *    i.e. distances [W + b*L, W + (b+1)*L) with the same L as above.
+ *  - COWA_MODE_SINK_LOCAL: no long-range window (L = 0), i.e. sliding-window
+ *    attention with sinks, the related band-less pattern ("Sliding Window
+ *    Attention Beats Linear Attention ...", SWA with attention sinks).
+ *
  * Conventions.
  *  - Every device pointer is owned by the caller.  The library never
  *    allocates or frees device memory and never synchronises; work is
@@ -53,7 +62,7 @@ typedef enum {
   COWA_ERR_CAPACITY = 6       /* caller's plan buffers are too small */
 } cowa_status;
 
-enum { COWA_MODE_COWA = 0, COWA_MODE_CAUSAL = 1 };
+enum { COWA_MODE_COWA = 0, COWA_MODE_CAUSAL = 1, COWA_MODE_SINK_LOCAL = 2 };
 enum { COWA_DTYPE_BF16 = 0, COWA_DTYPE_F32 = 1 };
 
 /* Position-only pattern (mechanism paragraph of the news page; Abstract).
@@ -66,7 +75,9 @@ enum { COWA_DTYPE_BF16 = 0, COWA_DTYPE_F32 = 1 };
  *  h_kv_global    KV heads over all tensor-parallel ranks (>= 1)
  *  kv_head_offset global index of this caller's first KV head (tensor
  *                 parallelism keeps the bands complementary across ranks)
- *  mode           COWA_MODE_COWA or COWA_MODE_CAUSAL */
+ *  mode           COWA_MODE_COWA, COWA_MODE_CAUSAL or COWA_MODE_SINK_LOCAL
+ *  n_bands        distinct long-range windows, 0 <= n_bands <= h_kv_global;
+ *                 0 means h_kv_global (CoWA proper) */
 typedef struct {
   int32_t n_ctx;
   int32_t sink;
@@ -75,6 +86,7 @@ typedef struct {
   int32_t h_kv_global;
   int32_t kv_head_offset;
   int32_t mode;
+  int32_t n_bands;
 } cowa_pattern;
 
 /* Human-readable name of a status code (static storage). */

@@ -57,6 +57,7 @@ import numpy as np
 
 MODE_COWA = 0
 MODE_CAUSAL = 1
+MODE_SINK_LOCAL = 2
 
 
 @dataclass(frozen=True)
@@ -70,7 +71,14 @@ class Pattern:
     h_kv_global: number of KV heads across all tensor-parallel ranks.
     kv_head_offset: global index of this rank's first KV head ([SF] sixth
         paragraph: bands follow the global KV-head index).
-    mode: MODE_COWA or MODE_CAUSAL (dense causal FullAttn, [AB] Abstract).
+    mode: MODE_COWA, MODE_CAUSAL (dense causal FullAttn, [AB] Abstract) or
+        MODE_SINK_LOCAL (sink and local windows only: sliding-window attention
+        with sinks, the band-less pattern of the [BH] page).
+    n_bands: number of distinct long-range windows shared out over the
+        h_kv_global heads ([SF] ablation paragraph: 1, 2, 4 or 8 distinct
+        windows over 8 KV heads at fixed per-head width).  0 means
+        h_kv_global (CoWA proper).  Head g takes window g mod n_bands, of
+        width L as above (the page does not say which head takes which).
     """
 
     n_ctx: int
@@ -80,6 +88,7 @@ class Pattern:
     h_kv_global: int = 1
     kv_head_offset: int = 0
     mode: int = MODE_COWA
+    n_bands: int = 0
 
 
 def band_length(n_ctx: int, window: int, h_kv_global: int) -> int:
@@ -93,7 +102,17 @@ def band_length(n_ctx: int, window: int, h_kv_global: int) -> int:
 
 
 def resolved_band(p: Pattern) -> int:
+    """Band width L; 0 (no band) in MODE_SINK_LOCAL."""
+    if p.mode == MODE_SINK_LOCAL:
+        return 0
     return p.band if p.band > 0 else band_length(p.n_ctx, p.window, p.h_kv_global)
+
+
+def band_index(g: int, p: Pattern) -> int:
+    """Which long-range window global KV head g takes: g itself for CoWA,
+    g mod n_bands for the duplicated-window ablation."""
+    m = p.n_bands if p.n_bands > 0 else p.h_kv_global
+    return g % m
 
 
 def visible(t, j, g, p: Pattern):
@@ -112,8 +131,9 @@ def visible(t, j, g, p: Pattern):
     in_sink = j < p.sink
     in_local = dist < p.window
     if L > 0:
-        lo = p.window + g * L
-        hi = p.window + (g + 1) * L
+        bi = band_index(g, p)
+        lo = p.window + bi * L
+        hi = p.window + (bi + 1) * L
         in_band = (dist >= lo) & (dist < hi)
     else:
         in_band = np.zeros(np.broadcast(t, j).shape, dtype=bool)
@@ -144,9 +164,11 @@ def visible_intervals(t: int, g: int, p: Pattern):
             ivs.append((0, min(p.sink, t + 1)))
         ivs.append((max(0, t - p.window + 1), t + 1))
         if L > 0:
-            # distances [W+gL, W+(g+1)L)  <=>  keys (t-W-(g+1)L, t-W-gL]
-            a = t - (p.window + (g + 1) * L) + 1
-            b = t - (p.window + g * L) + 1
+            # distances [W+bL, W+(b+1)L)  <=>  keys (t-W-(b+1)L, t-W-bL], b the
+            # head's window index
+            bi = band_index(g, p)
+            a = t - (p.window + (bi + 1) * L) + 1
+            b = t - (p.window + bi * L) + 1
             a, b = max(a, 0), min(b, t + 1)
             if a < b:
                 ivs.append((a, b))
@@ -236,8 +258,9 @@ def tile_counts_intervals_fast(n: int, g: int, p: Pattern, bm: int, bn: int) -> 
         loc = (loc_a, np.maximum(t + 1, loc_a))
         ivs = [sink, loc]
         if L > 0:
-            ba = np.maximum(t - (p.window + (g + 1) * L) + 1, sink_b)
-            bb = np.minimum(t - (p.window + g * L) + 1, loc_a)
+            bi = band_index(g, p)
+            ba = np.maximum(t - (p.window + (bi + 1) * L) + 1, sink_b)
+            bb = np.minimum(t - (p.window + bi * L) + 1, loc_a)
             bb = np.maximum(bb, ba)
             ivs.append((ba, bb))
     counts = np.zeros((nqt, nkt), dtype=np.int64)

@@ -25,6 +25,7 @@ COWA_ERR_HIP = 5
 COWA_ERR_CAPACITY = 6
 COWA_MODE_COWA = 0
 COWA_MODE_CAUSAL = 1
+COWA_MODE_SINK_LOCAL = 2
 COWA_DTYPE_BF16 = 0
 COWA_DTYPE_F32 = 1
 
@@ -43,12 +44,13 @@ class CowaError(RuntimeError):
 class cowa_pattern(ctypes.Structure):
     _fields_ = [("n_ctx", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("band", ctypes.c_int32), ("h_kv_global", ctypes.c_int32),
-                ("kv_head_offset", ctypes.c_int32), ("mode", ctypes.c_int32)]
+                ("kv_head_offset", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("n_bands", ctypes.c_int32)]
 
 
 def make_pattern(n_ctx, sink, window, band=0, h_kv_global=1, kv_head_offset=0,
-                 mode=COWA_MODE_COWA) -> cowa_pattern:
-    return cowa_pattern(n_ctx, sink, window, band, h_kv_global, kv_head_offset, mode)
+                 mode=COWA_MODE_COWA, n_bands=0) -> cowa_pattern:
+    return cowa_pattern(n_ctx, sink, window, band, h_kv_global, kv_head_offset, mode, n_bands)
 
 
 _lib = None

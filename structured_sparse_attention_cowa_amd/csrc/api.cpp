@@ -8,16 +8,25 @@ namespace cowa {
 
 cowa_status validate_pattern(const cowa_pattern* p, int32_t h_kv_local) {
   if (!p) return COWA_ERR_INVALID_ARG;
-  if (p->mode != COWA_MODE_COWA && p->mode != COWA_MODE_CAUSAL) return COWA_ERR_INVALID_ARG;
+  if (p->mode != COWA_MODE_COWA && p->mode != COWA_MODE_CAUSAL &&
+      p->mode != COWA_MODE_SINK_LOCAL)
+    return COWA_ERR_INVALID_ARG;
   if (p->n_ctx < 1 || p->sink < 0 || p->window < 1 || p->h_kv_global < 1 ||
       p->kv_head_offset < 0)
     return COWA_ERR_INVALID_ARG;
   if (h_kv_local < 1 || (int64_t)p->kv_head_offset + h_kv_local > p->h_kv_global)
     return COWA_ERR_INVALID_ARG;
+  if (p->n_bands < 0 || p->n_bands > p->h_kv_global) return COWA_ERR_INVALID_ARG;
   return COWA_OK;
 }
 
+// Distinct long-range windows: n_bands, or one per global KV head.
+int32_t resolve_n_bands(const cowa_pattern* p) {
+  return p->n_bands > 0 ? p->n_bands : p->h_kv_global;
+}
+
 int32_t resolve_band(const cowa_pattern* p) {
+  if (p->mode == COWA_MODE_SINK_LOCAL) return 0;
   return p->band > 0 ? p->band : derive_band(p->n_ctx, p->window, p->h_kv_global);
 }
 
@@ -89,7 +98,8 @@ static cowa_status plan_size_memo(const cowa_pattern* p, int32_t n, int32_t h_kv
     if (e.used && e.n == n && e.h == h_kv_local && e.bm == bm && e.bn == bn &&
         e.p.n_ctx == p->n_ctx && e.p.sink == p->sink && e.p.window == p->window &&
         e.p.band == p->band && e.p.h_kv_global == p->h_kv_global &&
-        e.p.kv_head_offset == p->kv_head_offset && e.p.mode == p->mode) {
+        e.p.kv_head_offset == p->kv_head_offset && e.p.mode == p->mode &&
+        e.p.n_bands == p->n_bands) {
       *nnz = e.nnz;
       return COWA_OK;
     }
@@ -157,6 +167,7 @@ extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   fp.band = resolve_band(p);
   fp.kv_head_offset = p->kv_head_offset;
   fp.causal = p->mode == COWA_MODE_CAUSAL;
+  fp.n_bands = resolve_n_bands(p);
   fp.scale = softmax_scale;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_fwd(fp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
@@ -220,6 +231,7 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
   dp.band = resolve_band(p);
   dp.kv_head_offset = p->kv_head_offset;
   dp.causal = p->mode == COWA_MODE_CAUSAL;
+  dp.n_bands = resolve_n_bands(p);
   dp.chunk = geo.chunk;
   dp.n_splits = geo.n_splits;
   dp.o_f32 = o_dtype == COWA_DTYPE_F32;
@@ -375,6 +387,7 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   bp.band = resolve_band(p);
   bp.kv_head_offset = p->kv_head_offset;
   bp.causal = p->mode == COWA_MODE_CAUSAL;
+  bp.n_bands = resolve_n_bands(p);
   bp.o_f32 = o_dtype == COWA_DTYPE_F32;
   bp.g_f32 = g_dtype == COWA_DTYPE_F32;
   bp.scale = softmax_scale;

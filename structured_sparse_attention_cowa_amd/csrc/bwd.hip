@@ -193,7 +193,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const int qi = p.nqt - 1 - rem / p.Hq;  // heavy first
   const int hq = rem - (rem / p.Hq) * p.Hq;
   const int h = hq / p.G;
-  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
+                                      band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
   const int q_row = qi * QBM + wave * 32 + l32;
   const int q_row_c = q_row < p.N ? q_row : p.N - 1;
@@ -429,7 +430,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     b = rem / p.Hkv;
     h = rem - b * p.Hkv;
   }
-  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
+                                      band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
   const int key = kj * KBN + wave * 32 + l32;
   const int key_c = key < p.N ? key : p.N - 1;

@@ -21,6 +21,7 @@ constexpr int kDecodeMaxGroup = 8;
 
 cowa_status validate_pattern(const cowa_pattern* p, int32_t h_kv_local);
 int32_t resolve_band(const cowa_pattern* p);
+int32_t resolve_n_bands(const cowa_pattern* p);
 
 cowa_status plan_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int32_t bm,
                       int32_t bn, int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t cap,
@@ -41,6 +42,7 @@ struct FwdParams {
   int64_t os_b, os_t, os_h;
   int32_t B, N, Hq, Hkv, G, nqt;
   int32_t sink, window, band, kv_head_offset, causal;
+  int32_t n_bands;  // distinct long-range windows (head g takes g mod n_bands)
   float scale;       // softmax scale (natural-log domain)
   float scale_log2;  // scale * log2(e)
 };
@@ -73,6 +75,7 @@ struct DecodeParams {
   int64_t os_b, os_h;
   int32_t B, Hq, Hkv, G, n_max;
   int32_t sink, window, band, kv_head_offset, causal;
+  int32_t n_bands;  // distinct long-range windows (head g takes g mod n_bands)
   int32_t chunk, n_splits;
   int32_t o_f32;
   float scale;
@@ -118,6 +121,7 @@ struct BwdParams {
   int32_t n_sink_tiles;  // leading key tiles whose step lists are split (0: none)
   int32_t nch;           // parts per split key tile
   int32_t sink, window, band, kv_head_offset, causal;
+  int32_t n_bands;  // distinct long-range windows (head g takes g mod n_bands)
   int32_t o_f32, g_f32;
   float scale;
   float scale_log2;

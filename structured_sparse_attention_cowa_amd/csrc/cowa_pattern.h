@@ -8,7 +8,9 @@
 // history is cut into non-overlapping long-range bands, one per global KV
 // head.  The band partition used here (the pages give no formula):
 //   L = ceil((n_ctx - W) / H_kv_global) if n_ctx > W else 0,
-//   head g sees distances t - j in [W + g*L, W + (g+1)*L).
+//   head g sees distances t - j in [W + b*L, W + (b+1)*L) with b = g for
+//   CoWA, b = g mod m for the duplicated-window ablation with m distinct
+//   windows (news page, ablation paragraph); L = 0 for sink + local only.
 #pragma once
 
 #include <stdint.h>
@@ -30,6 +32,10 @@ COWA_HD int32_t derive_band(int32_t n_ctx, int32_t window, int32_t h_kv_global) 
   return (int32_t)((rest + h_kv_global - 1) / h_kv_global);
 }
 
+// Long-range window index of global KV head g when m distinct windows are
+// shared out over the heads (m = h_kv_global: CoWA, every head its own).
+COWA_HD int32_t band_slot(int32_t g, int32_t m) { return m > 0 ? g % m : g; }
+
 // Parameters of one global KV head, with the band bounds expressed as
 // distances.  Band distances [band_lo, band_hi); band_hi == band_lo when L == 0.
 struct HeadPattern {
@@ -40,13 +46,14 @@ struct HeadPattern {
   int32_t causal;  // 1: dense causal mode
 };
 
-COWA_HD HeadPattern head_pattern(int32_t sink, int32_t window, int32_t band, int32_t g,
+// b: the head's long-range window index (band_slot of its global index)
+COWA_HD HeadPattern head_pattern(int32_t sink, int32_t window, int32_t band, int32_t b,
                                  int32_t causal) {
   HeadPattern h;
   h.sink = sink;
   h.window = window;
   // distances can exceed int32 only for absurd n_ctx; clamp in 64-bit
-  int64_t lo = (int64_t)window + (int64_t)g * band;
+  int64_t lo = (int64_t)window + (int64_t)b * band;
   int64_t hi = lo + band;
   h.band_lo = lo > 0x3fffffff ? 0x3fffffff : (int32_t)lo;
   h.band_hi = hi > 0x3fffffff ? 0x3fffffff : (int32_t)hi;

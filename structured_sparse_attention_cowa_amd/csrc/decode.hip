@@ -88,7 +88,8 @@ __device__ __forceinline__ Segs decode_segs(const DecodeParams& p, int b, int h,
   int len = p.seqlens[b];
   len = len < 1 ? 1 : (len > p.n_max ? p.n_max : len);
   const int t = len - 1;
-  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
+                                      band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
   const RowRanges rr = row_ranges(hp, t);
   Segs s;
   s.lo0 = rr.lo[0];

@@ -97,7 +97,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const int qi = p.nqt - 1 - rem / p.Hq;
   const int hq = rem - (rem / p.Hq) * p.Hq;
   const int h = hq / p.G;
-  const HeadPattern hp = head_pattern(p.sink, p.window, p.band, p.kv_head_offset + h, p.causal);
+  const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
+                                      band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
   const int q_row = qi * BM + wave * 32 + l32;
   const int q_row_c = q_row < p.N ? q_row : p.N - 1;

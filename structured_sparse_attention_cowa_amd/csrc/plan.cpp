@@ -34,8 +34,9 @@ cowa_status plan_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int3
   int64_t nnz = 0;
   if (write) row_ptr[0] = 0;
   for (int32_t h = 0; h < h_kv_local; ++h) {
-    const HeadPattern hp =
-        head_pattern(p->sink, p->window, L, p->kv_head_offset + h, p->mode == COWA_MODE_CAUSAL);
+    const HeadPattern hp = head_pattern(p->sink, p->window, L,
+                                        band_slot(p->kv_head_offset + h, resolve_n_bands(p)),
+                                        p->mode == COWA_MODE_CAUSAL);
     for (int32_t qi = 0; qi < nqt; ++qi) {
       const int32_t r0 = qi * bm;
       const int32_t r1 = imin(r0 + bm, n);

@@ -56,14 +56,16 @@ class Prefill:
     """Device-resident prefill problem: inputs, plan and outputs."""
 
     def __init__(self, x: W.PrefillInputs, sink, window, h_kv_global, offset=0, mode=0,
-                 n_ctx=None, o_dtype="f32"):
+                 n_ctx=None, o_dtype="f32", n_bands=0):
         import torch
         self.x = x
         B, N, Hq, d = x.q_bits.shape
         Hkv = x.k_bits.shape[2]
         self.B, self.N, self.Hq, self.Hkv, self.d = B, N, Hq, Hkv, d
-        self.pattern = C.make_pattern(n_ctx or N, sink, window, 0, h_kv_global, offset, mode)
-        self.opattern = O.Pattern(n_ctx or N, sink, window, 0, h_kv_global, offset, mode)
+        self.pattern = C.make_pattern(n_ctx or N, sink, window, 0, h_kv_global, offset, mode,
+                                      n_bands)
+        self.opattern = O.Pattern(n_ctx or N, sink, window, 0, h_kv_global, offset, mode,
+                                  n_bands)
         self.bm, self.bn = C.cowa_fwd_block_sizes(d)
         rp, col, fl = C.cowa_plan(self.pattern, N, Hkv, self.bm, self.bn)
         self.nnz = len(col)
@@ -123,9 +125,10 @@ class Backward:
     the upstream gradient, both plans, the workspace and the gradients."""
 
     def __init__(self, x: W.PrefillInputs, sink, window, h_kv_global, offset=0, mode=0,
-                 n_ctx=None, o_dtype="f32", g_dtype="f32", do_seed=1):
+                 n_ctx=None, o_dtype="f32", g_dtype="f32", do_seed=1, n_bands=0):
         import torch
-        self.pf = pf = Prefill(x, sink, window, h_kv_global, offset, mode, n_ctx, o_dtype)
+        self.pf = pf = Prefill(x, sink, window, h_kv_global, offset, mode, n_ctx, o_dtype,
+                               n_bands)
         B, N, Hq, Hkv, d = pf.B, pf.N, pf.Hq, pf.Hkv, pf.d
         self.do_bits = W.grad_output(do_seed, B, N, Hq, d)
         self.do = bits_to_dev(self.do_bits)

@@ -122,7 +122,7 @@ def test_plan_capacity_and_invalid(lib):
                      fl.ctypes.data, nnz - 1)
     assert st == C.COWA_ERR_CAPACITY
     bad = [dict(window=0), dict(sink=-1), dict(h_kv_global=0), dict(kv_head_offset=2),
-           dict(mode=2), dict(n_ctx=0)]
+           dict(mode=3), dict(n_ctx=0)]
     for b in bad:
         cpb, _ = pat(**b)
         out = ctypes.c_int64()
