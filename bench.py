@@ -258,7 +258,27 @@ def main():
                                         "mfma_frac": round(sl_flops / (sl_ms * 1e-3) / 1e12
                                                            / PEAK_BF16_TFLOPS, 4)},
                     "ablation_8k": ablation_8k(C, W, torch, dev, to_dev, time_it)}
+        # decode on windowed caches (each KV head keeps its sink and a ring of
+        # the positions later queries can still see)
+        rows, total_rows = C.cowa_kv_window_rows(pd, wd.H_kv, wd.n_max)
+        kw = torch.empty((wd.B, total_rows, wd.d), dtype=torch.bfloat16, device=dev)
+        vw = torch.empty_like(kw)
+        C.cowa_kv_window_fill(pd, kc, vc, sl, kw, vw)
+        dec_win_ms = time_it(lambda: C.cowa_decode_window(pd, qd, kw, vw, sl, od, lsed, wd.H_kv,
+                                                          wd.n_max, 1.0 / np.sqrt(wd.d), ws), 5)
+        del kw, vw
+        decode_window = {
+            "us": round(dec_win_ms * 1e3, 2),
+            "tokens_per_s": round(wd.B / (dec_win_ms * 1e-3), 1),
+            "hbm_frac": round(dec_bytes / (dec_win_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kv_rows_per_sequence": int(total_rows),
+            "full_cache_rows_per_sequence": wd.H_kv * wd.n_max,
+            "memory_ratio_all_heads": round(wd.H_kv * wd.n_max / total_rows, 3),
+            "rows_per_head": [int(r) for r in rows],
+            "memory_ratio_per_rank": [round(wd.n_max / int(r), 3) for r in rows],
+        }
         extras = {
+            "decode_window": decode_window,
             "variants": variants,
             "prefill_per_g": [{"g": g, "ms": round(per_g[g], 4),
                                "tflops": round(flops[g] / (per_g[g] * 1e-3) / 1e12, 1),

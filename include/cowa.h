@@ -173,6 +173,51 @@ cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cach
                         const int64_t strides[10], float softmax_scale,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- windowed KV cache for decode ---------------------------------------
+ * Per-rank decode memory well below FullAttn's ("CoWindow Attention: Full
+ * Causal Coverage Is a Collective Property", Abstract) follows from the
+ * pattern: local KV head h (long-range window b = g mod n_bands, g its global
+ * index) never again reads a non-sink key at distance >= W + (b+1) L from the
+ * newest query.  Its retained cache is S' = min(S, n_max) sink rows followed by
+ * a ring of R_h = min(W + (b+1) L, n_max - S') rows; position j >= S' lives in
+ * ring row (j - S') mod R_h.  A sequence's windowed cache stacks the local
+ * heads in order: rows_h = S' + R_h rows each, every row d contiguous bf16
+ * values; k_win and v_win are [B, total_rows, d] with a per-sequence stride
+ * (elements) of at least total_rows * d.  COWA_MODE_CAUSAL keeps everything
+ * and returns COWA_ERR_UNSUPPORTED. */
+
+/* Rows per local head (head_rows[h_kv_local], may be NULL) and per sequence. */
+cowa_status cowa_kv_window_rows(const cowa_pattern* p, int32_t h_kv_local, int32_t n_max,
+                                int32_t* head_rows, int64_t* total_rows);
+
+/* Pack the retained rows of full caches [B, n_max, H_kv_local, d] (strides[0..5]:
+ * k b,t,h and v b,t,h) for lengths cache_seqlens (device int32[B]) into k_win,
+ * v_win (strides[6], strides[7]: their per-sequence strides).  Ring rows that
+ * hold no position yet are zeroed. */
+cowa_status cowa_kv_window_fill(const cowa_pattern* p, const void* k_cache,
+                                const void* v_cache, const int32_t* cache_seqlens,
+                                void* k_win, void* v_win, int32_t B, int32_t H_kv_local,
+                                int32_t d, int32_t n_max, const int64_t strides[8],
+                                void* stream);
+
+/* Write one new token per sequence: k_new, v_new [B, H_kv_local, d] (strides[0..3]:
+ * k b,h and v b,h) go to position cache_seqlens[b] - 1 (the length after the
+ * append); strides[4], strides[5]: per-sequence strides of k_win, v_win. */
+cowa_status cowa_kv_window_append(const cowa_pattern* p, const void* k_new, const void* v_new,
+                                  const int32_t* cache_seqlens, void* k_win, void* v_win,
+                                  int32_t B, int32_t H_kv_local, int32_t d, int32_t n_max,
+                                  const int64_t strides[6], void* stream);
+
+/* cowa_decode against windowed caches: same result as cowa_decode on the full
+ * caches the windowed ones were built from.  strides: q b,h; k_win b; v_win b;
+ * o b,h.  Workspace as cowa_decode_workspace_size. */
+cowa_status cowa_decode_window(const cowa_pattern* p, const void* q, const void* k_win,
+                               const void* v_win, const int32_t* cache_seqlens, void* o,
+                               int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
+                               int32_t H_kv_local, int32_t d, int32_t n_max,
+                               const int64_t strides[6], float softmax_scale, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* ---- cowa_bwd: backward of the prefill (training) operator -------------
  * The pages report the backward latency of the training operator next to
  * the forward ("CoWindow Attention: Full Causal Coverage Is a Collective

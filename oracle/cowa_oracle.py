@@ -387,6 +387,19 @@ def decode_visible_keys(t: int, g: int, p: Pattern) -> np.ndarray:
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
+def retained_mask(n_max: int, g: int, p: Pattern) -> np.ndarray:
+    """R[t, j] = key j <= t is visible to some query t' with t <= t' < n_max.
+
+    What a decode cache must still hold for head g after the token at
+    position t has been appended ([NX] Abstract: lower decode memory; the
+    pattern is fixed by positions, so later queries are known in advance).
+    Brute force over the dense mask: a suffix OR over query rows.
+    """
+    m = visible_mask(n_max, n_max, g, p)
+    later = np.logical_or.accumulate(m[::-1], axis=0)[::-1]
+    return later & (np.arange(n_max)[None, :] <= np.arange(n_max)[:, None])
+
+
 def visible_pairs(n: int, g: int, p: Pattern) -> int:
     """Sum over rows t < n of |vis_g(t)| (element-level work of one head)."""
     return int(sum(visible_count(t, g, p) for t in range(n)))

@@ -32,7 +32,8 @@ COWA_DTYPE_F32 = 1
 EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa_plan_size",
             "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode",
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
-            "cowa_bwd_workspace_size", "cowa_bwd")
+            "cowa_bwd_workspace_size", "cowa_bwd", "cowa_kv_window_rows",
+            "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window")
 
 
 class CowaError(RuntimeError):
@@ -103,6 +104,16 @@ def load():
     lib.cowa_bwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, i32, i32,
                              vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
                              i32, i32, i32, i32, i32, P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_kv_window_rows.restype = ctypes.c_int
+    lib.cowa_kv_window_rows.argtypes = [pat, i32, i32, vp, P(i64)]
+    lib.cowa_kv_window_fill.restype = ctypes.c_int
+    lib.cowa_kv_window_fill.argtypes = [pat, vp, vp, vp, vp, vp, i32, i32, i32, i32, P(i64), vp]
+    lib.cowa_kv_window_append.restype = ctypes.c_int
+    lib.cowa_kv_window_append.argtypes = [pat, vp, vp, vp, vp, vp, i32, i32, i32, i32, P(i64),
+                                          vp]
+    lib.cowa_decode_window.restype = ctypes.c_int
+    lib.cowa_decode_window.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                       P(i64), f32, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -307,3 +318,61 @@ def cowa_bwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block
                          float(softmax_scale), workspace.data_ptr(),
                          workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check(st, "cowa_bwd")
+
+
+def cowa_kv_window_rows(p: cowa_pattern, h_kv_local: int, n_max: int):
+    """(rows per local head as an int32 array, rows per sequence)."""
+    rows = np.zeros(h_kv_local, dtype=np.int32)
+    total = ctypes.c_int64()
+    _check(load().cowa_kv_window_rows(ctypes.byref(p), h_kv_local, n_max, rows.ctypes.data,
+                                      ctypes.byref(total)), "cowa_kv_window_rows")
+    return rows, total.value
+
+
+def _win_stride(t):
+    assert t.dim() == 3 and t.stride(2) == 1 and t.stride(1) == t.shape[2], \
+        "windowed caches are [B, rows, d] with contiguous rows"
+    return t.stride(0)
+
+
+def cowa_kv_window_fill(p: cowa_pattern, k_cache, v_cache, cache_seqlens, k_win, v_win,
+                        stream=None):
+    """Pack full caches [B, n_max, H_kv, d] into windowed caches [B, rows, d]."""
+    B, n_max, Hkv, d = k_cache.shape
+    strides = (ctypes.c_int64 * 8)(*(_strides(k_cache, 3) + _strides(v_cache, 3)
+                                     + [_win_stride(k_win), _win_stride(v_win)]))
+    _check(load().cowa_kv_window_fill(ctypes.byref(p), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      cache_seqlens.data_ptr(), k_win.data_ptr(),
+                                      v_win.data_ptr(), B, Hkv, d, n_max, strides,
+                                      _stream_ptr(stream)), "cowa_kv_window_fill")
+
+
+def cowa_kv_window_append(p: cowa_pattern, k_new, v_new, cache_seqlens, k_win, v_win, n_max,
+                          stream=None):
+    """Write k_new, v_new [B, H_kv, d] at position cache_seqlens - 1."""
+    B, Hkv, d = k_new.shape
+    strides = (ctypes.c_int64 * 6)(*(_strides(k_new, 2) + _strides(v_new, 2)
+                                     + [_win_stride(k_win), _win_stride(v_win)]))
+    _check(load().cowa_kv_window_append(ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(),
+                                        cache_seqlens.data_ptr(), k_win.data_ptr(),
+                                        v_win.data_ptr(), B, Hkv, d, n_max, strides,
+                                        _stream_ptr(stream)), "cowa_kv_window_append")
+
+
+def cowa_decode_window(p: cowa_pattern, q, k_win, v_win, cache_seqlens, o, lse, h_kv_local,
+                       n_max, softmax_scale: float, workspace, stream=None):
+    """Decode against windowed caches [B, rows, d]; q/o [B, H_q, d], lse [B, H_q]."""
+    import torch
+    if q.dtype != torch.bfloat16 or k_win.dtype != torch.bfloat16:
+        raise TypeError("q and windowed caches must be bfloat16")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    B, Hq, d = q.shape
+    strides = (ctypes.c_int64 * 6)(*(_strides(q, 2) + [_win_stride(k_win), _win_stride(v_win)]
+                                     + _strides(o, 2)))
+    _check(load().cowa_decode_window(ctypes.byref(p), q.data_ptr(), k_win.data_ptr(),
+                                     v_win.data_ptr(), cache_seqlens.data_ptr(), o.data_ptr(),
+                                     _o_dtype(o), lse.data_ptr(), B, Hq, h_kv_local, d, n_max,
+                                     strides, float(softmax_scale), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(stream)), "cowa_decode_window")

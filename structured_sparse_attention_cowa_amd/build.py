@@ -27,7 +27,7 @@ COMMON = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["plan.cpp", "api.cpp", "fwd.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "fwd.hip", "decode.hip", "bwd.hip", "kvwin.hip"]
 
 
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{os.path.join(ROOT, 'include')}",

@@ -185,21 +185,24 @@ extern "C" cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t
   return COWA_OK;
 }
 
-extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cache,
-                                   const void* v_cache, const int32_t* cache_seqlens, void* o,
-                                   int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
-                                   int32_t H_kv_local, int32_t d, int32_t n_max,
-                                   const int64_t strides[10], float softmax_scale,
-                                   void* workspace, size_t ws_bytes, void* stream) {
+// Decode against a full cache (win = 0: strides[2..7] = k b,t,h and v b,t,h)
+// or against the windowed layout (win = 1: rows of d contiguous values,
+// strides[2] and strides[5] = the per-sequence stride of k_win and v_win).
+static cowa_status decode_impl(const cowa_pattern* p, const void* q, const void* k,
+                               const void* v, const int32_t* cache_seqlens, void* o,
+                               int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
+                               int32_t H_kv_local, int32_t d, int32_t n_max,
+                               const int64_t strides[10], float softmax_scale, void* workspace,
+                               size_t ws_bytes, void* stream, int win) {
   cowa_status st = validate_pattern(p, H_kv_local);
   if (st != COWA_OK) return st;
-  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse || !strides)
-    return COWA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cache_seqlens || !o || !lse || !strides) return COWA_ERR_INVALID_ARG;
   if (B < 1 || H_q < 1 || n_max < 1 || H_q % H_kv_local != 0) return COWA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
   if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 10)) return COWA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  if (win && p->mode == COWA_MODE_CAUSAL) return COWA_ERR_UNSUPPORTED;
   const int32_t G = H_q / H_kv_local;
   if (G > kDecodeMaxGroup) return COWA_ERR_UNSUPPORTED;
   const DecodeGeometry geo = decode_geometry(p, B, H_q, H_kv_local, d, n_max);
@@ -210,8 +213,8 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
 
   DecodeParams dp;
   dp.q = static_cast<const uint16_t*>(q);
-  dp.k = static_cast<const uint16_t*>(k_cache);
-  dp.v = static_cast<const uint16_t*>(v_cache);
+  dp.k = static_cast<const uint16_t*>(k);
+  dp.v = static_cast<const uint16_t*>(v);
   dp.seqlens = cache_seqlens;
   dp.o = o;
   dp.lse = lse;
@@ -235,9 +238,139 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
   dp.chunk = geo.chunk;
   dp.n_splits = geo.n_splits;
   dp.o_f32 = o_dtype == COWA_DTYPE_F32;
+  dp.win = win;
   dp.scale = softmax_scale;
   dp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_decode(dp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* cache_seqlens, void* o,
+                                   int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
+                                   int32_t H_kv_local, int32_t d, int32_t n_max,
+                                   const int64_t strides[10], float softmax_scale,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, cache_seqlens, o, o_dtype, lse, B, H_q, H_kv_local,
+                     d, n_max, strides, softmax_scale, workspace, ws_bytes, stream, 0);
+}
+
+// ---- windowed KV cache ----
+
+static cowa_status window_rows(const cowa_pattern* p, int32_t h_kv_local, int32_t n_max,
+                               int32_t* head_rows, int64_t* total, int32_t* max_rows) {
+  cowa_status st = validate_pattern(p, h_kv_local);
+  if (st != COWA_OK) return st;
+  if (n_max < 1) return COWA_ERR_INVALID_ARG;
+  if (p->mode == COWA_MODE_CAUSAL) return COWA_ERR_UNSUPPORTED;
+  const int32_t L = resolve_band(p);
+  const int32_t m = resolve_n_bands(p);
+  const int32_t s_rows = window_sink_rows(p->sink, n_max);
+  int64_t sum = 0;
+  int32_t mx = 0;
+  for (int32_t h = 0; h < h_kv_local; ++h) {
+    const int32_t r =
+        s_rows + window_ring_rows(p->sink, p->window, L, band_slot(p->kv_head_offset + h, m), n_max);
+    if (head_rows) head_rows[h] = r;
+    sum += r;
+    mx = r > mx ? r : mx;
+  }
+  if (total) *total = sum;
+  if (max_rows) *max_rows = mx;
+  return COWA_OK;
+}
+
+extern "C" cowa_status cowa_kv_window_rows(const cowa_pattern* p, int32_t h_kv_local,
+                                           int32_t n_max, int32_t* head_rows,
+                                           int64_t* total_rows) {
+  if (!total_rows) return COWA_ERR_INVALID_ARG;
+  return window_rows(p, h_kv_local, n_max, head_rows, total_rows, nullptr);
+}
+
+static cowa_status kvwin_common(const cowa_pattern* p, int32_t B, int32_t H_kv_local, int32_t d,
+                                int32_t n_max, const int64_t* win_strides, KvWinParams* kp,
+                                int32_t* max_rows) {
+  int64_t total = 0;
+  cowa_status st = window_rows(p, H_kv_local, n_max, nullptr, &total, max_rows);
+  if (st != COWA_OK) return st;
+  if (B < 1 || B > 65535 || H_kv_local > 65535) return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  // each sequence's rows must fit its stride
+  if (win_strides[0] < total * d || win_strides[1] < total * d) return COWA_ERR_INVALID_ARG;
+  kp->kw_b = win_strides[0];
+  kp->vw_b = win_strides[1];
+  kp->B = B;
+  kp->Hkv = H_kv_local;
+  kp->d = d;
+  kp->n_max = n_max;
+  kp->sink = p->sink;
+  kp->window = p->window;
+  kp->band = resolve_band(p);
+  kp->kv_head_offset = p->kv_head_offset;
+  kp->n_bands = resolve_n_bands(p);
+  return COWA_OK;
+}
+
+extern "C" cowa_status cowa_kv_window_fill(const cowa_pattern* p, const void* k_cache,
+                                           const void* v_cache, const int32_t* cache_seqlens,
+                                           void* k_win, void* v_win, int32_t B,
+                                           int32_t H_kv_local, int32_t d, int32_t n_max,
+                                           const int64_t strides[8], void* stream) {
+  if (!k_cache || !v_cache || !cache_seqlens || !k_win || !v_win || !strides)
+    return COWA_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 8)) return COWA_ERR_INVALID_ARG;
+  KvWinParams kp;
+  int32_t max_rows = 0;
+  cowa_status st = kvwin_common(p, B, H_kv_local, d, n_max, strides + 6, &kp, &max_rows);
+  if (st != COWA_OK) return st;
+  kp.k_src = static_cast<const uint16_t*>(k_cache);
+  kp.v_src = static_cast<const uint16_t*>(v_cache);
+  kp.seqlens = cache_seqlens;
+  kp.k_win = static_cast<uint16_t*>(k_win);
+  kp.v_win = static_cast<uint16_t*>(v_win);
+  kp.ks_b = strides[0]; kp.ks_t = strides[1]; kp.ks_h = strides[2];
+  kp.vs_b = strides[3]; kp.vs_t = strides[4]; kp.vs_h = strides[5];
+  if (max_rows == 0) return COWA_OK;
+  return launch_kv_window_fill(kp, max_rows, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_kv_window_append(const cowa_pattern* p, const void* k_new,
+                                             const void* v_new, const int32_t* cache_seqlens,
+                                             void* k_win, void* v_win, int32_t B,
+                                             int32_t H_kv_local, int32_t d, int32_t n_max,
+                                             const int64_t strides[6], void* stream) {
+  if (!k_new || !v_new || !cache_seqlens || !k_win || !v_win || !strides)
+    return COWA_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 6)) return COWA_ERR_INVALID_ARG;
+  KvWinParams kp;
+  cowa_status st = kvwin_common(p, B, H_kv_local, d, n_max, strides + 4, &kp, nullptr);
+  if (st != COWA_OK) return st;
+  kp.k_src = static_cast<const uint16_t*>(k_new);
+  kp.v_src = static_cast<const uint16_t*>(v_new);
+  kp.seqlens = cache_seqlens;
+  kp.k_win = static_cast<uint16_t*>(k_win);
+  kp.v_win = static_cast<uint16_t*>(v_win);
+  kp.ks_b = strides[0]; kp.ks_t = 0; kp.ks_h = strides[1];
+  kp.vs_b = strides[2]; kp.vs_t = 0; kp.vs_h = strides[3];
+  return launch_kv_window_append(kp, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_decode_window(const cowa_pattern* p, const void* q, const void* k_win,
+                                          const void* v_win, const int32_t* cache_seqlens,
+                                          void* o, int32_t o_dtype, float* lse, int32_t B,
+                                          int32_t H_q, int32_t H_kv_local, int32_t d,
+                                          int32_t n_max, const int64_t strides[6],
+                                          float softmax_scale, void* workspace, size_t ws_bytes,
+                                          void* stream) {
+  if (!strides) return COWA_ERR_INVALID_ARG;
+  int64_t total = 0;
+  cowa_status st = window_rows(p, H_kv_local, n_max, nullptr, &total, nullptr);
+  if (st != COWA_OK) return st;
+  if (strides[2] < total * d || strides[3] < total * d) return COWA_ERR_INVALID_ARG;
+  // windowed rows are d contiguous values; the head offset is a row offset
+  const int64_t full[10] = {strides[0], strides[1], strides[2], d, 0,
+                            strides[3], d, 0, strides[4], strides[5]};
+  return decode_impl(p, q, k_win, v_win, cache_seqlens, o, o_dtype, lse, B, H_q, H_kv_local, d,
+                     n_max, full, softmax_scale, workspace, ws_bytes, stream, 1);
 }
 
 extern "C" cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n) {

@@ -78,6 +78,7 @@ struct DecodeParams {
   int32_t n_bands;  // distinct long-range windows (head g takes g mod n_bands)
   int32_t chunk, n_splits;
   int32_t o_f32;
+  int32_t win;  // 1: K/V in the windowed layout (rows [B][heads x (sink + ring)][d])
   float scale;
   float scale_log2;
 };
@@ -130,6 +131,22 @@ struct BwdParams {
 // Launchers return a hipError_t value (0 on success).
 int launch_fwd(const FwdParams& p, int d, int o_f32, void* stream);
 int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream);
+
+// Windowed KV cache (fill from a full cache / append one token).
+struct KvWinParams {
+  const uint16_t* k_src;  // fill: full cache [B, n_max, H_kv, d]; append: [B, H_kv, d]
+  const uint16_t* v_src;
+  const int32_t* seqlens;
+  uint16_t* k_win;  // [B, rows, d], rows = heads x (sink rows + ring rows)
+  uint16_t* v_win;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t kw_b, vw_b;
+  int32_t B, Hkv, d, n_max;
+  int32_t sink, window, band, kv_head_offset, n_bands;
+};
+int launch_kv_window_fill(const KvWinParams& p, int max_head_rows, void* stream);
+int launch_kv_window_append(const KvWinParams& p, void* stream);
 int launch_bwd(const BwdParams& p, int d, void* stream);
 
 }  // namespace cowa

@@ -107,6 +107,24 @@ COWA_HD int32_t row_count(const RowRanges& r) {
   return (r.hi[0] - r.lo[0]) + (r.hi[1] - r.lo[1]) + (r.hi[2] - r.lo[2]);
 }
 
+// Windowed KV cache for decode ("CoWindow Attention: Full Causal Coverage Is
+// a Collective Property", Abstract: lower per-rank decode memory).  For query
+// t, head g with long-range window b sees non-sink keys only at distances
+// t - j < W + (b+1) L, and later queries see even newer keys, so keys at
+// larger distances (other than the sink) are never read again.  A head's
+// retained cache is its sink rows followed by a ring of
+//   R = min(W + (b+1) L, n_max - S')     (S' = min(S, n_max))
+// rows; position j >= S' lives in ring row (j - S') mod R.  Visible keys are
+// closer than R to the query, so two of them never share a ring row.
+COWA_HD int32_t window_sink_rows(int32_t sink, int32_t n_max) { return imin(sink, n_max); }
+
+COWA_HD int32_t window_ring_rows(int32_t sink, int32_t window, int32_t band, int32_t b,
+                                 int32_t n_max) {
+  const int64_t want = (int64_t)window + ((int64_t)b + 1) * band;
+  const int64_t cap = (int64_t)n_max - window_sink_rows(sink, n_max);
+  return (int32_t)(want < cap ? want : cap);
+}
+
 // Largest number of keys any row can see: bounds the decode split count.
 COWA_HD int32_t max_row_count(int32_t sink, int32_t window, int32_t band, int32_t causal,
                               int32_t n_keys) {

@@ -75,6 +75,19 @@ __device__ __forceinline__ float wave_max_of_groups8(float m) {
 
 struct Segs {
   int lo0, n0, lo1, n1, lo2, n2;
+  // windowed layout (ring > 0): ring rows follow s_rows sink rows; rs1, rs2
+  // are the ring rows of the band and local ranges' first keys
+  int ring, s_rows, rs1, rs2;
+  // cache row of the v-th visible key (its position in the full layout);
+  // each non-sink range is at most one ring long, so it wraps at most once
+  __device__ int row(int v) const {
+    if (ring == 0) return key(v);
+    if (v < n0) return lo0 + v;
+    v -= n0;
+    int r = v < n1 ? rs1 + v : rs2 + (v - n1);
+    r = r >= ring ? r - ring : r;
+    return s_rows + r;
+  }
   __device__ int key(int v) const {
     if (v < n0) return lo0 + v;
     v -= n0;
@@ -98,8 +111,30 @@ __device__ __forceinline__ Segs decode_segs(const DecodeParams& p, int b, int h,
   s.n1 = rr.hi[1] - rr.lo[1];
   s.lo2 = rr.lo[2];
   s.n2 = rr.hi[2] - rr.lo[2];
+  s.ring = 0;
+  s.s_rows = 0;
+  s.rs1 = s.rs2 = 0;
+  if (p.win) {
+    s.s_rows = window_sink_rows(p.sink, p.n_max);
+    s.ring = window_ring_rows(p.sink, p.window, p.band,
+                              band_slot(p.kv_head_offset + h, p.n_bands), p.n_max);
+    if (s.ring > 0) {
+      s.rs1 = s.n1 > 0 ? (s.lo1 - s.s_rows) % s.ring : 0;
+      s.rs2 = s.n2 > 0 ? (s.lo2 - s.s_rows) % s.ring : 0;
+    }
+  }
   *t_out = t;
   return s;
+}
+
+// First row of local KV head h in a windowed cache (heads are stacked).
+__device__ __forceinline__ int64_t window_head_row(const DecodeParams& p, int h) {
+  const int s_rows = window_sink_rows(p.sink, p.n_max);
+  int64_t r = 0;
+  for (int i = 0; i < h; ++i)
+    r += s_rows + window_ring_rows(p.sink, p.window, p.band,
+                                   band_slot(p.kv_head_offset + i, p.n_bands), p.n_max);
+  return r;
 }
 
 template <int D, int G>
@@ -134,8 +169,9 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
-  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+  const int64_t hrow = p.win ? window_head_row(p, h) : 0;
+  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (p.win ? hrow * p.ks_t : (int64_t)h * p.ks_h);
+  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (p.win ? hrow * p.vs_t : (int64_t)h * p.vs_h);
 
   // ---- phase A: scores ----
   {
@@ -158,7 +194,7 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
       for (int u = 0; u < UA; ++u) {
         const int kk = base + NWAVES * KPA * u;
         if (kk < cnt) {
-          const int key = sg.key(v0 + kk);
+          const int key = sg.row(v0 + kk);
           const uint16_t* kp = kbase + (int64_t)key * p.ks_t + part * DPL;
 #pragma unroll
           for (int i = 0; i < NVA; ++i) kr[u][i] = ldg16(kp + 8 * i);
@@ -253,7 +289,7 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
       for (int u = 0; u < UC; ++u) {
         const int kk = base + NWAVES * KPW * u;
         if (kk < cnt) {
-          const int key = sg.key(v0 + kk);
+          const int key = sg.row(v0 + kk);
           vr[u] = ldg16(vbase + (int64_t)key * p.vs_t + dp * 8);
         }
       }
