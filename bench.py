@@ -278,6 +278,7 @@ def main():
             "memory_ratio_per_rank": [round(wd.n_max / int(r), 3) for r in rows],
         }
         extras = {
+            "varlen_prefill": varlen_prefill(C, W, torch, dev, time_it),
             "decode_window": decode_window,
             "variants": variants,
             "prefill_per_g": [{"g": g, "ms": round(per_g[g], 4),
@@ -393,6 +394,40 @@ def ablation_8k(C, W, torch, dev, to_dev, time_it):
                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
     return out
+
+
+def varlen_prefill(C, W, torch, dev, time_it):
+    """Packed prefill of 8 sequences of seeded lengths in [4096, 32768] (the
+    32K workload's heads: H_q=40, H_kv=8, d=128, S=128, W=4096, L=3584)."""
+    w = W.VARLEN32K
+    lens = w.lengths()
+    T, max_len = int(lens.sum()), int(lens.max())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    q = torch.randn((T, w.H_q, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((T, w.H_kv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((T, w.H_kv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    o = torch.empty((T, w.H_q, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.H_q, T), dtype=torch.float32, device=dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    p = C.make_pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
+    bm, bn = C.cowa_fwd_block_sizes(w.d)
+    rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, max_len, w.H_kv, bm, bn)]
+    ms = time_it(lambda: C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
+                                           cu, max_len, 1.0 / np.sqrt(w.d)), 5)
+    band = C.cowa_band_length(p)
+    G = w.H_q // w.H_kv
+    pairs = 0
+    for n in lens:
+        t = np.arange(int(n))
+        pairs += sum(int(visible_counts(t, g, w.sink, w.window, band).sum())
+                     for g in range(w.H_kv))
+    flops = 4.0 * w.d * G * pairs
+    return {"workload": f"{w.n_seqs} packed sequences, lengths {[int(x) for x in lens]} "
+                        f"({T} tokens), H_q=40, H_kv=8, d=128, S=128, W=4096, L={band}",
+            "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def cpu_baseline(x, wp, scale, target_s=12.0):

@@ -145,6 +145,26 @@ cowa_status cowa_fwd(const cowa_pattern* p,
                      int32_t B, int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
                      const int64_t strides[12], float softmax_scale, void* stream);
 
+/* Packed ("varlen") prefill: n_seqs sequences of different lengths back to
+ * back in one launch, a second workload shape of the same operator (used in
+ * training and inference, Abstract).  Sequence b is at token rows
+ * [cu_seqlens[b], cu_seqlens[b+1]) of q, o [total_tokens, H_q, d] and k, v
+ * [total_tokens, H_kv_local, d]; positions t restart at 0 in every sequence.
+ *  cu_seqlens     device int32[n_seqs + 1], cu_seqlens[0] = 0, nondecreasing,
+ *                 last = total_tokens, every length <= max_seqlen (not
+ *                 checked on the host: rows past max_seqlen are not computed)
+ *  plan           cowa_plan for n = max_seqlen (one plan serves every length:
+ *                 visibility depends on positions only)
+ *  lse            fp32 [H_q, total_tokens]
+ *  strides        element strides (t, h) of q, k, v, o (8). */
+cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_row_ptr,
+                            const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                            int32_t block_m, int32_t block_n, const void* q, const void* k,
+                            const void* v, void* o, int32_t o_dtype, float* lse,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                            int32_t total_tokens, int32_t H_q, int32_t H_kv_local, int32_t d,
+                            const int64_t strides[8], float softmax_scale, void* stream);
+
 /* ---- cowa_decode: one query token per sequence --------------------------
  * Sequence b's new token sits at position t_b = cache_seqlens[b] - 1 (its own
  * K/V are already in the cache) and attends to vis_g(t_b) among cached keys

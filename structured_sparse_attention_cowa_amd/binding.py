@@ -33,7 +33,8 @@ EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa
             "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode",
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
             "cowa_bwd_workspace_size", "cowa_bwd", "cowa_kv_window_rows",
-            "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window")
+            "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window",
+            "cowa_fwd_varlen")
 
 
 class CowaError(RuntimeError):
@@ -114,6 +115,9 @@ def load():
     lib.cowa_decode_window.restype = ctypes.c_int
     lib.cowa_decode_window.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                        P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_fwd_varlen.restype = ctypes.c_int
+    lib.cowa_fwd_varlen.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, P(i64), f32, vp]
     _lib = lib
     return lib
 
@@ -376,3 +380,31 @@ def cowa_decode_window(p: cowa_pattern, q, k_win, v_win, cache_seqlens, o, lse, 
                                      strides, float(softmax_scale), workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(),
                                      _stream_ptr(stream)), "cowa_decode_window")
+
+
+def cowa_fwd_varlen(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
+                    q, k, v, o, lse, cu_seqlens, max_seqlen: int, softmax_scale: float,
+                    stream=None):
+    """Packed prefill: q/o [T, H_q, d], k/v [T, H_kv, d], lse [H_q, T], cu_seqlens
+    int32 [n_seqs + 1] on the device; the plan is built for n = max_seqlen."""
+    import torch
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v must be bfloat16 GPU tensors")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise TypeError("cu_seqlens must be an int32 GPU tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(lse.shape) != (Hq, T) or tuple(o.shape) != (T, Hq, d):
+        raise ValueError("o must be [T, H_q, d] and lse [H_q, T]")
+    strides = (ctypes.c_int64 * 8)(*(_strides(q, 2) + _strides(k, 2) + _strides(v, 2)
+                                     + _strides(o, 2)))
+    st = load().cowa_fwd_varlen(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(),
+                                flags.data_ptr(), nnz, block_m, block_n, q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), o.data_ptr(), _o_dtype(o),
+                                lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                max_seqlen, T, Hq, Hkv, d, strides, float(softmax_scale),
+                                _stream_ptr(stream))
+    _check(st, "cowa_fwd_varlen")

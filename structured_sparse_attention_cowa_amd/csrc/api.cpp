@@ -117,12 +117,15 @@ static bool strides_ok(const int64_t* s, int n) {
   return true;
 }
 
-extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
-                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
-                                int32_t block_m, int32_t block_n, const void* q, const void* k,
-                                const void* v, void* o, int32_t o_dtype, float* lse, int32_t B,
-                                int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
-                                const int64_t strides[12], float softmax_scale, void* stream) {
+// Prefill forward, batched (cu_seqlens NULL: [B, N, ...] with b strides) or
+// packed (cu_seqlens: B sequences of length <= N at rows cu_seqlens[b]..).
+static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, const int32_t* d_col,
+                            const uint8_t* d_flags, int64_t nnz, int32_t block_m,
+                            int32_t block_n, const void* q, const void* k, const void* v,
+                            void* o, int32_t o_dtype, float* lse, int32_t B, int32_t N,
+                            int32_t H_q, int32_t H_kv_local, int32_t d,
+                            const int64_t strides[12], float softmax_scale,
+                            const int32_t* cu_seqlens, int32_t total_tokens, void* stream) {
   cowa_status st = validate_pattern(p, H_kv_local);
   if (st != COWA_OK) return st;
   if (!d_row_ptr || !d_col || !d_flags || !q || !k || !v || !o || !lse || !strides)
@@ -168,9 +171,39 @@ extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   fp.kv_head_offset = p->kv_head_offset;
   fp.causal = p->mode == COWA_MODE_CAUSAL;
   fp.n_bands = resolve_n_bands(p);
+  fp.cu_seqlens = cu_seqlens;
+  fp.total_tokens = total_tokens;
   fp.scale = softmax_scale;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_fwd(fp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
+                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                                int32_t block_m, int32_t block_n, const void* q, const void* k,
+                                const void* v, void* o, int32_t o_dtype, float* lse, int32_t B,
+                                int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
+                                const int64_t strides[12], float softmax_scale, void* stream) {
+  return fwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, q, k, v, o, o_dtype, lse,
+                  B, N, H_q, H_kv_local, d, strides, softmax_scale, nullptr, 0, stream);
+}
+
+extern "C" cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_row_ptr,
+                                       const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                                       int32_t block_m, int32_t block_n, const void* q,
+                                       const void* k, const void* v, void* o, int32_t o_dtype,
+                                       float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
+                                       int32_t max_seqlen, int32_t total_tokens, int32_t H_q,
+                                       int32_t H_kv_local, int32_t d, const int64_t strides[8],
+                                       float softmax_scale, void* stream) {
+  if (!cu_seqlens || !strides) return COWA_ERR_INVALID_ARG;
+  if (n_seqs < 1 || total_tokens < 1 || max_seqlen < 1) return COWA_ERR_INVALID_ARG;
+  // token rows: (t, h) strides; the per-sequence offset comes from cu_seqlens
+  const int64_t full[12] = {0, strides[0], strides[1], 0, strides[2], strides[3],
+                            0, strides[4], strides[5], 0, strides[6], strides[7]};
+  return fwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, q, k, v, o, o_dtype, lse,
+                  n_seqs, max_seqlen, H_q, H_kv_local, d, full, softmax_scale, cu_seqlens,
+                  total_tokens, stream);
 }
 
 extern "C" cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,

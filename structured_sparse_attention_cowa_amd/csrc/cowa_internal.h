@@ -43,6 +43,11 @@ struct FwdParams {
   int32_t B, N, Hq, Hkv, G, nqt;
   int32_t sink, window, band, kv_head_offset, causal;
   int32_t n_bands;  // distinct long-range windows (head g takes g mod n_bands)
+  // packed sequences (varlen): B sequences, sequence b at token rows
+  // [cu_seqlens[b], cu_seqlens[b+1]) of length <= N; LSE [H_q, total_tokens].
+  // NULL: the batched layout ([B, N, ...] with the b strides).
+  const int32_t* cu_seqlens;
+  int32_t total_tokens;
   float scale;       // softmax scale (natural-log domain)
   float scale_log2;  // scale * log2(e)
 };

@@ -89,23 +89,38 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
-  // heavy-first order: later query tiles see more keys
-  const int per_b = p.nqt * p.Hq;
+  // heavy-first order over the whole batch: later query tiles see more keys
+  const int per_qi = p.B * p.Hq;
   const int wg = blockIdx.x;
-  const int b = wg / per_b;
-  const int rem = wg - b * per_b;
-  const int qi = p.nqt - 1 - rem / p.Hq;
-  const int hq = rem - (rem / p.Hq) * p.Hq;
+  const int qi = p.nqt - 1 - wg / per_qi;
+  const int rem = wg - (wg / per_qi) * per_qi;
+  const int b = rem / p.Hq;
+  const int hq = rem - b * p.Hq;
   const int h = hq / p.G;
+
+  // this sequence's length and the offsets of its rows
+  int N = p.N;
+  int64_t qb = (int64_t)b * p.qs_b, kb = (int64_t)b * p.ks_b, vb = (int64_t)b * p.vs_b;
+  int64_t ob = (int64_t)b * p.os_b, lse_base = ((int64_t)b * p.Hq + hq) * p.N;
+  if (p.cu_seqlens) {
+    const int start = p.cu_seqlens[b];
+    N = min(p.cu_seqlens[b + 1] - start, p.N);
+    if (qi * BM >= N) return;  // the whole workgroup: this tile is past the sequence
+    qb = (int64_t)start * p.qs_t;
+    kb = (int64_t)start * p.ks_t;
+    vb = (int64_t)start * p.vs_t;
+    ob = (int64_t)start * p.os_t;
+    lse_base = (int64_t)hq * p.total_tokens + start;
+  }
   const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
                                       band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
   const int q_row = qi * BM + wave * 32 + l32;
-  const int q_row_c = q_row < p.N ? q_row : p.N - 1;
+  const int q_row_c = q_row < N ? q_row : N - 1;
 
   bf16x8 qf[NK];
   {
-    const uint16_t* qp = p.q + (int64_t)b * p.qs_b + (int64_t)q_row_c * p.qs_t + (int64_t)hq * p.qs_h;
+    const uint16_t* qp = p.q + qb + (int64_t)q_row_c * p.qs_t + (int64_t)hq * p.qs_h;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks + 8 * hl));
@@ -124,8 +139,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const int row = h * p.nqt + qi;
   const int e0 = p.row_ptr[row];
   const int e1 = p.row_ptr[row + 1];
-  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
-  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+  const uint16_t* kbase = p.k + kb + (int64_t)h * p.ks_h;
+  const uint16_t* vbase = p.v + vb + (int64_t)h * p.vs_h;
 
   // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
   // holds row P / CPR, column chunk (P % CPR) ^ swizzle(row).  Per-lane
@@ -146,7 +161,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, const int* col,
                        int kj, uint16_t* dst) {
     const int key0 = kj * BN;
-    if (key0 + BN <= p.N) {
+    if (key0 + BN <= N) {
       const uint16_t* t = base + (int64_t)key0 * stride;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) g2lds16(t + off[i], dst + (wave * LOADS + i) * 512);
@@ -154,7 +169,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
-        key = key < p.N ? key : p.N - 1;
+        key = key < N ? key : N - 1;
         g2lds16(base + (int64_t)key * stride + col[i], dst + (wave * LOADS + i) * 512);
       }
     }
@@ -347,10 +362,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   }
 
   const float l_tot = pair_sum(l_run);
-  if (q_row < p.N) {
+  if (q_row < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* obase = reinterpret_cast<char*>(p.o);
-    const int64_t oidx = (int64_t)b * p.os_b + (int64_t)q_row * p.os_t + (int64_t)hq * p.os_h;
+    const int64_t oidx = ob + (int64_t)q_row * p.os_t + (int64_t)hq * p.os_h;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -367,7 +382,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       }
     if (hl == 0) {
       const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : NEG_INF;
-      p.lse[((int64_t)b * p.Hq + hq) * p.N + q_row] = lse;
+      p.lse[lse_base + q_row] = lse;
     }
   }
 }

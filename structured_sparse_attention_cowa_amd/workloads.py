@@ -96,6 +96,32 @@ D128K = DecodeWorkload("decode-128k", B=16, n_max=131072, n_ctx=131072, H_q=40, 
 PREFILL_WORKLOADS = (TINY, P8K, P32K, P128K)
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed prefill: n_seqs sequences with lengths uniform on [len_lo, len_hi]
+    (integers, drawn first), the 32K workload's heads and pattern."""
+    name: str
+    n_seqs: int
+    len_lo: int
+    len_hi: int
+    n_ctx: int
+    H_q: int
+    H_kv: int
+    d: int
+    sink: int
+    window: int
+    h_kv_global: int
+    seed: int
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.Generator(np.random.PCG64(self.seed))
+        return rng.integers(self.len_lo, self.len_hi, endpoint=True, size=self.n_seqs)
+
+
+VARLEN32K = VarlenWorkload("varlen-32k", n_seqs=8, len_lo=4096, len_hi=32768, n_ctx=32768,
+                           H_q=40, H_kv=8, d=128, sink=128, window=4096, h_kv_global=8, seed=6)
+
+
 @dataclass
 class PrefillInputs:
     q_bits: np.ndarray   # uint16 [B, N, H_q, d]
