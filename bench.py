@@ -402,14 +402,9 @@ def varlen_prefill(C, W, torch, dev, time_it):
     w = W.VARLEN32K
     lens = w.lengths()
     T, max_len = int(lens.sum()), int(lens.max())
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
-    q = torch.randn((T, w.H_q, w.d), generator=gen, device=dev).to(torch.bfloat16)
-    k = torch.randn((T, w.H_kv, w.d), generator=gen, device=dev).to(torch.bfloat16)
-    v = torch.randn((T, w.H_kv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    q, k, v, cu = W.varlen_device(w, dev)
     o = torch.empty((T, w.H_q, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.H_q, T), dtype=torch.float32, device=dev)
-    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
     p = C.make_pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
     bm, bn = C.cowa_fwd_block_sizes(w.d)
     rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, max_len, w.H_kv, bm, bn)]

@@ -147,7 +147,8 @@ cowa_status cowa_fwd(const cowa_pattern* p,
 
 /* Packed ("varlen") prefill: n_seqs sequences of different lengths back to
  * back in one launch, a second workload shape of the same operator (used in
- * training and inference, Abstract).  Sequence b is at token rows
+ * training and inference, "CoWindow Attention: Full Causal Coverage Is a
+ * Collective Property", Abstract).  Sequence b is at token rows
  * [cu_seqlens[b], cu_seqlens[b+1]) of q, o [total_tokens, H_q, d] and k, v
  * [total_tokens, H_kv_local, d]; positions t restart at 0 in every sequence.
  *  cu_seqlens     device int32[n_seqs + 1], cu_seqlens[0] = 0, nondecreasing,

@@ -219,3 +219,20 @@ def decode_cache_device(w: DecodeWorkload, lens: np.ndarray, device="cuda"):
             t[b, int(lens[b]):] = float("nan")
         caches.append(t)
     return caches[0], caches[1]
+
+
+def varlen_device(w: VarlenWorkload, device="cuda"):
+    """Packed Q [T, H_q, d], K, V [T, H_kv, d] bf16, N(0,1), drawn on the device
+    with torch's generator seeded w.seed (in the order Q, K, V), and
+    cu_seqlens int32 [n_seqs + 1] on the device; T = sum of w.lengths()."""
+    import torch
+
+    lens = w.lengths()
+    T = int(lens.sum())
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    q = torch.randn((T, w.H_q, w.d), generator=gen, device=device).to(torch.bfloat16)
+    k = torch.randn((T, w.H_kv, w.d), generator=gen, device=device).to(torch.bfloat16)
+    v = torch.randn((T, w.H_kv, w.d), generator=gen, device=device).to(torch.bfloat16)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(device)
+    return q, k, v, cu

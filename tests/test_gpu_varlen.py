@@ -66,3 +66,47 @@ def test_varlen_against_oracle_and_single_runs(lib, case):
         torch.cuda.synchronize()
         assert np.array_equal(o1.cpu().numpy()[0], o[a:b]), f"seq {i}"
         assert np.array_equal(l1.cpu().numpy()[0], lse[:, a:b]), f"seq {i}"
+
+
+def test_varlen_32k_workload_sampled(lib):
+    """The packed 32K workload in the launch configuration bench.py times:
+    boundary and seeded rows of every sequence against the oracle, and every
+    sequence bit for bit against cowa_fwd on that sequence alone."""
+    import torch
+    from tests.gpu_helpers import sample_rows
+    w = W.VARLEN32K
+    lens = w.lengths()
+    T, max_len = int(lens.sum()), int(lens.max())
+    q, k, v, cu_d = W.varlen_device(w)
+    cu = cu_d.cpu().numpy()
+    p = C.make_pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
+    op = O.Pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
+    bm, bn = C.cowa_fwd_block_sizes(w.d)
+    rp, col, fl = [torch.from_numpy(a).cuda() for a in C.cowa_plan(p, max_len, w.H_kv, bm, bn)]
+    o = torch.full((T, w.H_q, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((w.H_q, T), float("nan"), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(w.d)
+    print(f"[varlen] {w.name} lens={list(lens)}", flush=True)
+    C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse, cu_d, max_len, scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    band = C.cowa_band_length(p)
+    heads = [0, 4, 5, 19, 20, 39]
+    for i, n in enumerate(lens):
+        a, b = int(cu[i]), int(cu[i + 1])
+        qs, ks, vs = q[a:b].unsqueeze(0), k[a:b].unsqueeze(0), v[a:b].unsqueeze(0)
+        rows = sample_rows(int(n), w.window, w.sink, band, w.h_kv_global, 4, 300 + i)
+        o_ref, lse_ref = O.attention(qs.float().cpu().numpy(), ks.float().cpu().numpy(),
+                                     vs.float().cpu().numpy(), op, scale, rows=rows, heads=heads)
+        og = o[a:b].cpu().numpy()[None]
+        lg = lse[:, a:b].cpu().numpy()[None]
+        check_close(og[:, rows][:, :, heads], lg[:, heads][:, :, rows], o_ref, lse_ref,
+                    f"{w.name} seq {i} (n={n})")
+        rp1, col1, fl1 = [torch.from_numpy(t).cuda()
+                          for t in C.cowa_plan(p, int(n), w.H_kv, bm, bn)]
+        o1 = torch.empty((1, int(n), w.H_q, w.d), dtype=torch.float32, device="cuda")
+        l1 = torch.empty((1, w.H_q, int(n)), dtype=torch.float32, device="cuda")
+        C.cowa_fwd(p, rp1, col1, fl1, col1.numel(), bm, bn, qs, ks, vs, o1, l1, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[a:b]), f"seq {i}"
+        assert torch.equal(l1[0], lse[:, a:b]), f"seq {i}"
