@@ -445,11 +445,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
       vf[ks] = __builtin_bit_cast(bf16x8, ldg16(vp + 16 * ks + 8 * hl));
     }
   }
+  // The accumulators start as the (zero) result of an MFMA rather than as
+  // zero constants: the compiler then keeps them in accumulator registers
+  // across the step loop, where the MFMAs update them in place (started from
+  // constants, every step copied all 128 values out to ordinary registers
+  // and back).
   f32x16 dk[ND], dv[ND];
+  {
+    const bf16x8 z = {};
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
+    for (int i = 0; i < ND; ++i) {
+      dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
+      dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
+    }
   }
 
   // steps run over (query head of the group, visible query tile); a part
@@ -614,11 +622,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int s = 0; s < nsteps; ++s) {
-    if (s & 1)
-      step(s, Q1, O1, S1, Q0, O0, S0);
-    else
-      step(s, Q0, O0, S0, Q1, O1, S1);
+  // unrolled by two so the buffers alternate with compile-time slots
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, Q0, O0, S0, Q1, O1, S1);
+    if (s + 1 < nsteps) step(s + 1, Q1, O1, S1, Q0, O0, S0);
   }
 
   if (part >= 0) {
