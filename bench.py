@@ -286,6 +286,13 @@ def main():
                                "mfma_frac": round(flops[g] / (per_g[g] * 1e-3) / 1e12
                                                   / PEAK_BF16_TFLOPS, 4)}
                               for g in range(wp.h_kv_global)],
+            # the eight g together are one tensor-parallel step's ranks run
+            # one after another on this GPU
+            "prefill_all_g": {"ms_sum": round(float(np.sum(per_g)), 4),
+                              "tflops": round(float(np.sum(flops)) / (np.sum(per_g) * 1e-3)
+                                              / 1e12, 1),
+                              "mfma_frac": round(float(np.sum(flops)) / (np.sum(per_g) * 1e-3)
+                                                 / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "prefill_causal_mode": {"ms": round(causal_ms, 4),
                                     "tflops": round(causal_flops / (causal_ms * 1e-3) / 1e12, 1),
                                     "cowa_speedup_g0": round(causal_ms / per_g[0], 3),
@@ -448,8 +455,17 @@ def cpu_baseline(x, wp, scale, target_s=12.0):
     t0 = time.perf_counter()
     O.attention(q, k, v, p, scale, rows=rows)
     dt = time.perf_counter() - t0
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{len(rows)} seeded random query rows (all 5 heads) of the 128K "
                       f"single-rank prefill at g=0, dense masked fp64 softmax, {dt:.1f} s"}
 
