@@ -48,6 +48,7 @@ struct FwdParams {
   // NULL: the batched layout ([B, N, ...] with the b strides).
   const int32_t* cu_seqlens;
   int32_t total_tokens;
+  int32_t xcd_chunk;  // workgroup order: chunks of this many go to one XCD (set by launch_fwd)
   float scale;       // softmax scale (natural-log domain)
   float scale_log2;  // scale * log2(e)
 };
