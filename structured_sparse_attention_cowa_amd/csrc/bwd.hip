@@ -37,6 +37,11 @@
 #include "cowa_internal.h"
 #include "kernel_util.h"
 
+// key tiles per XCD chunk of the dK/dV grid (the dQ grid takes up to 8 query
+// tiles): with 8, the K/V and Q/dO re-reads of neighbouring tiles mostly hit
+// the XCD's L2 (32 was slower, from L2 thrash across the chunk's span)
+constexpr int KV_CHUNK_TILES = 8;
+
 namespace cowa {
 namespace {
 
@@ -187,7 +192,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const int l32 = lane & 31;
 
   const int per_b = p.nqt * p.Hq;
-  const int wg = blockIdx.x;
+  const int wg = xcd_logical(blockIdx.x, p.xcd_chunk_q, p.B * per_b);
+  if (wg < 0) return;
   const int b = wg / per_b;
   const int rem = wg - b * per_b;
   const int qi = p.nqt - 1 - rem / p.Hq;  // heavy first
@@ -413,7 +419,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   // First the parts of the split sink key tiles, then the other key tiles in
   // ascending order (in causal mode the early ones carry the most query tiles).
   const int n_part_wg = p.B * p.Hkv * p.n_sink_tiles * p.nch;
-  int wg = blockIdx.x;
+  int wg = xcd_logical(blockIdx.x, p.xcd_chunk_kv,
+                       p.B * p.Hkv * (p.nkt_kv + p.n_sink_tiles * (p.nch - 1)));
+  if (wg < 0) return;
   int b, h, kj, part = -1;
   if (wg < n_part_wg) {
     part = wg % p.nch;
@@ -688,14 +696,19 @@ __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) 
 
 }  // namespace
 
-int launch_bwd(const BwdParams& p, int d, void* stream) {
+int launch_bwd(const BwdParams& p_in, int d, void* stream) {
   if (d != D) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // XCD chunks: up to 8 query tiles with all their heads (dQ); up to
+  // KV_CHUNK_TILES key tiles with all their (sequence, head) pairs (dK/dV)
+  BwdParams p = p_in;
+  const int64_t kv_units = p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1);
+  p.xcd_chunk_q = xcd_chunk(p.Hq, (int64_t)p.B * p.nqt, 8);
+  p.xcd_chunk_kv = xcd_chunk((int64_t)p.B * p.Hkv, kv_units, KV_CHUNK_TILES);
   hipLaunchKernelGGL(cowa_bwd_delta_kernel, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
                      dim3(256), 0, s, p);
-  const dim3 gq((unsigned)((int64_t)p.B * p.nqt * p.Hq));
-  const dim3 gk((unsigned)((int64_t)p.B * p.Hkv *
-                           (p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1))));
+  const dim3 gq((unsigned)xcd_grid((int64_t)p.B * p.nqt * p.Hq, p.xcd_chunk_q));
+  const dim3 gk((unsigned)xcd_grid((int64_t)p.B * p.Hkv * kv_units, p.xcd_chunk_kv));
   const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles * REDUCE_SPLIT), (unsigned)p.B);
   if (p.g_f32) {
     hipLaunchKernelGGL(cowa_bwd_dq_kernel<true>, gq, dim3(QTHREADS), 0, s, p);

@@ -11,6 +11,25 @@
 namespace cowa {
 
 // Prefill kernel tile: 8 wavefronts x 32 query rows, 64 keys per K/V tile.
+// Workgroup order dealt to the XCDs in chunks.  The dispatcher sends
+// workgroup i to XCD i mod kXcds; a kernel that maps i through xcd_logical
+// runs logical workgroups [c * chunk, (c + 1) * chunk) on XCD c mod kXcds, so
+// neighbours in the logical order (which read the same tiles) share an L2.
+constexpr int kXcds = 8;  // XCDs of an MI355X
+
+// chunk = units_per_chunk * per_unit, with units_per_chunk up to max_units
+// while every XCD still gets four chunks or more
+inline int32_t xcd_chunk(int64_t per_unit, int64_t units, int64_t max_units) {
+  int64_t k = units / (4 * kXcds);
+  k = k < 1 ? 1 : (k > max_units ? max_units : k);
+  return (int32_t)(per_unit * k);
+}
+// grid size: the logical count padded to whole rounds of kXcds chunks
+inline int64_t xcd_grid(int64_t total, int32_t chunk) {
+  const int64_t span = (int64_t)kXcds * chunk;
+  return (total + span - 1) / span * span;
+}
+
 constexpr int kFwdBlockM = 256;
 constexpr int kFwdBlockN = 64;
 
@@ -125,6 +144,7 @@ struct BwdParams {
   int64_t dvs_b, dvs_t, dvs_h;
   float* part;   // workspace: fp32 dK, dV partials of the split sink key tiles
   int32_t B, N, Hq, Hkv, G, nqt, nkt_kv, nqt_kv, npad;
+  int32_t xcd_chunk_q, xcd_chunk_kv;  // workgroup chunks per XCD (set by launch_bwd)
   int32_t n_sink_tiles;  // leading key tiles whose step lists are split (0: none)
   int32_t nch;           // parts per split key tile
   int32_t sink, window, band, kv_head_offset, causal;

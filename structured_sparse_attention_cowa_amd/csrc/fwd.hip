@@ -40,7 +40,6 @@ using namespace kern;
 constexpr int BM = kFwdBlockM;  // query rows per workgroup (32 per wavefront)
 constexpr int BN = kFwdBlockN;  // 64 keys per tile
 constexpr int NWAVES = BM / 32;
-constexpr int kXcds = 8;        // XCDs of an MI355X; workgroups are dealt round-robin
 constexpr int NTHREADS = 64 * NWAVES;
 
 // The running maximum is only raised when a row's maximum grows by more than
@@ -96,14 +95,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   // tiles with all their heads, which read the same K/V tiles) goes to XCD
   // c mod 8, so those reads share one L2.  Padding workgroups exit at once.
   const int per_qi = p.B * p.Hq;
-  int wg = blockIdx.x;
-  {
-    const int xcd = wg & (kXcds - 1);
-    const int r = wg / kXcds;
-    const int j = r / p.xcd_chunk;
-    wg = (j * kXcds + xcd) * p.xcd_chunk + (r - j * p.xcd_chunk);
-    if (wg >= per_qi * p.nqt) return;
-  }
+  const int wg = xcd_logical(blockIdx.x, p.xcd_chunk, per_qi * p.nqt);
+  if (wg < 0) return;
   const int qi = p.nqt - 1 - wg / per_qi;
   const int rem = wg - (wg / per_qi) * per_qi;
   const int b = rem / p.Hq;
@@ -402,16 +395,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 }  // namespace
 
 int launch_fwd(const FwdParams& p_in, int d, int o_f32, void* stream) {
-  // chunk = k query tiles with all their (sequence, head) pairs, k up to 8
-  // while every XCD still gets four chunks or more
+  // a chunk is up to 8 query tiles with all their (sequence, head) pairs
   FwdParams p = p_in;
   const int64_t per_qi = (int64_t)p.B * p.Hq;
-  int64_t k = p.nqt / (4 * kXcds);
-  k = k < 1 ? 1 : (k > 8 ? 8 : k);
-  p.xcd_chunk = (int32_t)(per_qi * k);
-  const int64_t span = (int64_t)kXcds * p.xcd_chunk;
-  const int64_t total = per_qi * p.nqt;
-  const dim3 grid((unsigned)((total + span - 1) / span * span));
+  p.xcd_chunk = xcd_chunk(per_qi, p.nqt, 8);
+  const dim3 grid((unsigned)xcd_grid(per_qi * p.nqt, p.xcd_chunk));
   const dim3 block(NTHREADS);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 128) {

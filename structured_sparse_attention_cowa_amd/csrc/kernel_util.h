@@ -10,6 +10,8 @@
 
 #include <stdint.h>
 
+#include "cowa_internal.h"
+
 namespace cowa {
 namespace kern {
 
@@ -29,6 +31,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Logical index of workgroup i under the chunked XCD order (see kXcds), or
+// -1 for a padding workgroup past total.
+__device__ __forceinline__ int xcd_logical(int i, int chunk, int total) {
+  const int xcd = i % kXcds;
+  const int r = i / kXcds;
+  const int j = r / chunk;
+  const int l = (j * kXcds + xcd) * chunk + (r - j * chunk);
+  return l < total ? l : -1;
 }
 
 // Lane l and lane l^32 hold the two halves of one accumulator column; this
