@@ -38,6 +38,10 @@
  *    the null stream).
  *  - Host-side validation returns an error before anything is launched.  A
  *    failed launch returns COWA_ERR_HIP.  Nothing throws across the ABI.
+ *  - Empty inputs: every count (B, N, H_q, H_kv_local, n_max, n_seqs,
+ *    total_tokens, max_seqlen) must be at least 1, else COWA_ERR_INVALID_ARG
+ *    and nothing runs.  Inside a packed (varlen) batch a sequence may be
+ *    empty (cu_seqlens[b+1] == cu_seqlens[b]); it produces no rows.
  *  - bf16 means IEEE bfloat16 stored as 2 bytes.  Strides are in elements;
  *    the last (head-dim) axis is always contiguous.
  *  - The library is stateless and thread-safe.

@@ -129,6 +129,9 @@ def test_bwd_host_validation(lib):
     assert _bwd_raw(lib, cp, bn_kv=64) == E.COWA_ERR_UNSUPPORTED
     assert _bwd_raw(lib, cp, d=64) == E.COWA_ERR_UNSUPPORTED
     assert _bwd_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
+    # empty inputs are rejected before anything runs
+    assert _bwd_raw(lib, cp, B=0, nnz=0, nnz_kv=0) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_raw(lib, cp, N=0, nnz=0, nnz_kv=0) == E.COWA_ERR_INVALID_ARG
     assert _bwd_raw(lib, cp, scale=float("inf")) == E.COWA_ERR_INVALID_ARG
     assert _bwd_raw(lib, cp, o_dtype=5) == E.COWA_ERR_INVALID_ARG
     assert _bwd_raw(lib, cp, g_dtype=5) == E.COWA_ERR_INVALID_ARG

@@ -177,6 +177,10 @@ def test_fwd_host_validation(lib):
     assert _fwd_raw(lib, cp, strides=[-1] + [1] * 11) == E.COWA_ERR_INVALID_ARG
     for nm in ("rp", "col", "fl", "q", "k", "v", "o", "lse"):
         assert _fwd_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
+    # empty inputs are rejected before anything runs
+    assert _fwd_raw(lib, cp, B=0, nnz=0) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, N=0, nnz=0) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, Hq=0, nnz=0) == E.COWA_ERR_INVALID_ARG
     cp3, _ = pat(n_ctx=256, h_kv_global=2, kv_head_offset=1)
     assert _fwd_raw(lib, cp3, nnz=1) == E.COWA_ERR_INVALID_ARG  # offset + H_kv_local > global
     # a plan built for another window has another size
@@ -211,6 +215,8 @@ def test_decode_host_validation(lib):
     assert call(scale=-1.0) == C.COWA_ERR_INVALID_ARG
     assert call(o_dtype=3) == C.COWA_ERR_INVALID_ARG
     assert call(nmax=0) == C.COWA_ERR_INVALID_ARG
+    assert call(B=0) == C.COWA_ERR_INVALID_ARG
+    assert call(Hq=0) == C.COWA_ERR_INVALID_ARG
 
 
 def test_single_hip_runtime_after_load(lib):
@@ -219,3 +225,39 @@ def test_single_hip_runtime_after_load(lib):
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def _varlen_raw(lib, cp, nnz=None, n_seqs=3, max_seqlen=300, total=700, Hq=4, Hkv=2, d=128,
+                null=None, scale=0.1, strides=None):
+    """cowa_fwd_varlen with fake (never dereferenced) device pointers."""
+    fake = ctypes.c_void_p(0x1000)
+    ptrs = {k: fake for k in ("rp", "col", "fl", "q", "k", "v", "o", "lse", "cu")}
+    if null:
+        ptrs[null] = None
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    if nnz is None:
+        nnz = C.cowa_plan_size(cp, max(max_seqlen, 1), Hkv, fbm, fbn)
+    arr = (ctypes.c_int64 * 8)(*(strides if strides is not None else [1] * 8))
+    return lib.cowa_fwd_varlen(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, fbm,
+                               fbn, ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], 1, ptrs["lse"],
+                               ptrs["cu"], n_seqs, max_seqlen, total, Hq, Hkv, d, arr, scale,
+                               None)
+
+
+def test_fwd_varlen_host_validation(lib):
+    cp, _ = pat(n_ctx=1024, h_kv_global=2)
+    E = C
+    assert _varlen_raw(lib, cp, n_seqs=0) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, total=0) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, max_seqlen=0) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
+    assert _varlen_raw(lib, cp, scale=-1.0) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, strides=[1] * 7 + [-1]) == E.COWA_ERR_INVALID_ARG
+    for nm in ("rp", "col", "fl", "q", "k", "v", "o", "lse", "cu"):
+        assert _varlen_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
+    # the plan must be the one for max_seqlen
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    other = C.cowa_plan_size(cp, 1024, 2, fbm, fbn)
+    assert other != C.cowa_plan_size(cp, 300, 2, fbm, fbn)
+    assert _varlen_raw(lib, cp, nnz=other) == E.COWA_ERR_PLAN_MISMATCH
