@@ -128,6 +128,32 @@ def test_decode_128k_workload_sampled(lib, mode):
         check_close(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, f"decode128k b={b} len={L}")
 
 
+def test_decode_128k_maximum_and_band_edge_lengths(lib):
+    """The 128K decode geometry (n_max = 131072, H_q=40, H_kv=8) at the
+    largest length (every earlier key visible, the last band ending exactly at
+    key 0) and where key 0 sits at the first distance of band 7 or the last of
+    band 6."""
+    import dataclasses
+    w = dataclasses.replace(W.D128K, B=3)
+    band = C.cowa_band_length(C.make_pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0))
+    edge = w.window + (w.h_kv_global - 1) * band      # distance where band 7 starts
+    lens = np.array([w.n_max, edge + 1, edge], np.int32)
+    rng = np.random.Generator(np.random.PCG64(123))
+    q_bits = W.to_bf16_bits(rng.standard_normal((w.B, w.H_q, w.d), dtype=np.float32))
+    k, v = W.decode_cache_device(w, lens)
+    print(f"[decode] 128K geometry lens={list(lens)}", flush=True)
+    o, lse = run_decode(q_bits, k, v, lens, w.sink, w.window, w.h_kv_global, w.n_ctx)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    p = O.Pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
+    for b in range(w.B):
+        L = int(lens[b])
+        kb = k[b:b + 1, :L].float().cpu().numpy()
+        vb = v[b:b + 1, :L].float().cpu().numpy()
+        o_ref, lse_ref = O.decode(W.bf16_bits_to_f32(q_bits[b:b + 1]), kb, vb, np.array([L]), p,
+                                  1.0 / np.sqrt(w.d))
+        check_close(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, f"decode128k edge len={L}")
+
+
 def test_decode_reuses_workspace(lib):
     """One workspace serves consecutive calls with different batches and
     lengths; a repeated call reproduces its first result bit for bit."""
