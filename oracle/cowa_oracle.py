@@ -22,7 +22,7 @@ sections, equations or listings):
        remaining history and, with the shared windows, their union gives full
        causal coverage; FullAttn is the dense comparison.
 
-Readings where the pages give no formula (each is listed in the design doc):
+Readings where the pages give no formula:
 
   * Band partition.  The pages state the structure but no formula.  This
     oracle fixes: with L = ceil((N_ctx - W) / H_kv_global) when N_ctx > W and
