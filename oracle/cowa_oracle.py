@@ -43,9 +43,13 @@ Parity status: the visibility predicate, interval form, tile lists and the
 masked softmax are pinned by the CPU tests (hand-derived 16-token grid,
 coverage/disjointness invariants, closed-form pair counts, reductions to
 textbook dense causal softmax, closed-form band-only case, softmax identities
-checked against scipy).  Numeric O/LSE values for the benchmark workloads are
-not printed by the pages; for those the definition below plus the reductions
-above are the only pins.
+checked against scipy).  The backward (attention_backward and its row- and
+key-sampled forms) is pinned by float64 autograd where CoWA reduces to dense
+causal attention, central finite differences of the forward, GQA sums of
+single-head problems and invariance to a common shift of the value rows; the
+KV retention mask by brute force over all later queries.  Numeric O/LSE
+values for the benchmark workloads are not printed by the pages; for those
+the definition below plus the reductions above are the pins.
 """
 
 from __future__ import annotations
