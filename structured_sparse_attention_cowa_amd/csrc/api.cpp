@@ -25,6 +25,13 @@ int32_t resolve_n_bands(const cowa_pattern* p) {
   return p->n_bands > 0 ? p->n_bands : p->h_kv_global;
 }
 
+// A grid of `total` workgroups in the chunked XCD order (chunks of at most 8
+// units of per_unit workgroups each) is padded to whole rounds of kXcds
+// chunks; the padded count must fit the 31-bit workgroup index.
+bool grid_fits(int64_t total, int64_t per_unit) {
+  return total + (int64_t)kXcds * 8 * per_unit <= 0x7fffffffLL;
+}
+
 int32_t resolve_band(const cowa_pattern* p) {
   if (p->mode == COWA_MODE_SINK_LOCAL) return 0;
   return p->band > 0 ? p->band : derive_band(p->n_ctx, p->window, p->h_kv_global);
@@ -140,7 +147,7 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
   if ((int64_t)block_n * strides[4] >= (1LL << 31) || (int64_t)block_n * strides[7] >= (1LL << 31))
     return COWA_ERR_UNSUPPORTED;
   const int64_t nqt = (N + block_m - 1) / block_m;
-  if ((int64_t)B * nqt * H_q > 0x7fffffffLL) return COWA_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)B * nqt * H_q, (int64_t)B * H_q)) return COWA_ERR_UNSUPPORTED;
   int64_t want = 0;
   st = plan_size_memo(p, N, H_kv_local, block_m, block_n, &want);
   if (st != COWA_OK) return st;
@@ -493,7 +500,8 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
     if ((int64_t)64 * strides[i] >= (1LL << 31)) return COWA_ERR_UNSUPPORTED;
   const int64_t nqt = (N + block_m - 1) / block_m;
   const int64_t nkt_kv = (N + block_n_kv - 1) / block_n_kv;
-  if ((int64_t)B * nqt * H_q > 0x7fffffffLL || (int64_t)B * H_kv_local * nkt_kv > 0x7fffffffLL ||
+  if (!grid_fits((int64_t)B * nqt * H_q, H_q) ||
+      !grid_fits((int64_t)B * H_kv_local * nkt_kv, (int64_t)B * H_kv_local) ||
       B > 65535 || H_q > 65535)
     return COWA_ERR_UNSUPPORTED;
   int64_t want = 0;
@@ -509,8 +517,8 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   if (st != COWA_OK) return st;
   if (!workspace || ws_bytes < geo.total_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return COWA_ERR_WORKSPACE;
-  if ((int64_t)B * H_kv_local * (nkt_kv + (int64_t)geo.n_sink_tiles * (geo.nch - 1)) >
-      0x7fffffffLL)
+  if (!grid_fits((int64_t)B * H_kv_local * (nkt_kv + (int64_t)geo.n_sink_tiles * (geo.nch - 1)),
+                 (int64_t)B * H_kv_local))
     return COWA_ERR_UNSUPPORTED;
 
   BwdParams bp;
