@@ -278,6 +278,8 @@ def main():
             "memory_ratio_per_rank": [round(wd.n_max / int(r), 3) for r in rows],
         }
         extras = {
+            "prefill_32k": prefill_32k(C, W, torch, dev, to_dev, time_it),
+            "prefill_8k": prefill_8k(C, W, torch, dev, to_dev, time_it),
             "varlen_prefill": varlen_prefill(C, W, torch, dev, time_it),
             "decode_window": decode_window,
             "variants": variants,
@@ -375,6 +377,50 @@ def main():
     }
     out.update(extras)
     print(json.dumps(out), flush=True)
+
+
+def _prefill_modes(C, W, torch, dev, to_dev, time_it, w):
+    """CoWA and full-causal prefill of one workload (all KV heads, offset 0)."""
+    x = W.prefill_inputs(w)
+    q, k, v = to_dev(x.q_bits), to_dev(x.k_bits), to_dev(x.v_bits)
+    o = torch.empty((w.B, w.N, w.H_q, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+    bm, bn = C.cowa_fwd_block_sizes(w.d)
+    G = w.H_q // w.H_kv
+    t = np.arange(w.N)
+    res = {}
+    for mode, name in ((0, "cowa"), (1, "causal")):
+        p = C.make_pattern(w.N, w.sink, w.window, 0, w.h_kv_global, 0, mode)
+        rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, w.N, w.H_kv, bm, bn)]
+        ms = time_it(lambda: C.cowa_fwd(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
+                                        1.0 / np.sqrt(w.d)), 5)
+        if mode == 0:
+            pairs = sum(int(visible_counts(t, g, w.sink, w.window, w.stated_band).sum())
+                        for g in range(w.H_kv))
+        else:
+            pairs = w.H_kv * w.N * (w.N + 1) // 2
+        flops = 4.0 * w.d * G * w.B * pairs
+        res[name] = {"ms": round(ms, 4), "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    res["cowa_speedup"] = round(res["causal"]["ms"] / res["cowa"]["ms"], 3)
+    return res
+
+
+def prefill_32k(C, W, torch, dev, to_dev, time_it):
+    """The 32K workload (B=1, N=32768, H_q=40, H_kv=8, d=128, S=128, W=4096,
+    L=3584, Q rows RMS 1.5), CoWA and full-causal mode."""
+    r = _prefill_modes(C, W, torch, dev, to_dev, time_it, W.P32K)
+    r["workload"] = "B=1, N=32768, H_q=40, H_kv=8, d=128, S=128, W=4096, L=3584"
+    return r
+
+
+def prefill_8k(C, W, torch, dev, to_dev, time_it):
+    """The 8K workload (B=2, N=8192, H_q=32, H_kv=8, d=128, S=64, W=1024,
+    L=896, 5% of keys x4), CoWA and full-causal mode."""
+    r = _prefill_modes(C, W, torch, dev, to_dev, time_it, W.P8K)
+    r["workload"] = "B=2, N=8192, H_q=32, H_kv=8, d=128, S=64, W=1024, L=896"
+    return r
 
 
 def ablation_8k(C, W, torch, dev, to_dev, time_it):
