@@ -261,7 +261,7 @@ cowa_status cowa_decode_window(const cowa_pattern* p, const void* q, const void*
  *  strides        element strides (b, t, h) of q, k, v, o, dout, dq, dk, dv (24)
  *  workspace      device scratch of cowa_bwd_workspace_size bytes (256-byte
  *                 aligned; no initialisation needed)
- *  d              128 (COWA_ERR_UNSUPPORTED otherwise).
+ *  d              64 or 128 (COWA_ERR_UNSUPPORTED otherwise).
  * Arithmetic: bf16 operands, fp32 accumulation; P and dS are rounded to bf16
  * before their products. */
 cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n);

@@ -415,7 +415,7 @@ extern "C" cowa_status cowa_decode_window(const cowa_pattern* p, const void* q, 
 
 extern "C" cowa_status cowa_bwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n) {
   if (!block_m || !block_n) return COWA_ERR_INVALID_ARG;
-  if (d != 128) return COWA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   *block_m = kBwdBlockM;
   *block_n = kBwdBlockN;
   return COWA_OK;
@@ -450,6 +450,7 @@ cowa_status bwd_geometry(const cowa_pattern* p, int32_t B, int32_t H_q, int32_t 
   const int32_t sink_tiles = (int32_t)(((int64_t)p->sink + kBwdBlockN - 1) / kBwdBlockN);
   g->n_sink_tiles = nch > 1 ? (sink_tiles < nkt ? sink_tiles : nkt) : 0;
   g->nch = g->n_sink_tiles > 0 ? (int32_t)nch : 1;
+  // partial rows are sized for the largest head dimension (128)
   const size_t part_bytes = (size_t)B * H_kv_local * g->n_sink_tiles * g->nch * 2 * kBwdBlockN *
                             128 * sizeof(float);
   g->total_bytes = g->part_offset + part_bytes;
@@ -490,7 +491,7 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (g_dtype != COWA_DTYPE_BF16 && g_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 24)) return COWA_ERR_INVALID_ARG;
-  if (d != 128) return COWA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (block_m != kFwdBlockM || block_n != kFwdBlockN || block_m_kv != kBwdBlockM ||
       block_n_kv != kBwdBlockN)
     return COWA_ERR_UNSUPPORTED;

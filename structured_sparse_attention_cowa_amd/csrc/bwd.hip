@@ -47,17 +47,18 @@ namespace {
 
 using namespace kern;
 
-constexpr int D = 128;
-constexpr int CPR = D / 8;  // 16-byte chunks per row
-constexpr int NK = D / 16;  // 16-deep k steps over the head dimension
-constexpr int ND = D / 32;  // 32-wide head-dimension blocks of an accumulator
+// Every kernel takes the head dimension D (64 or 128) as a template argument;
+// with it, CPR = D / 8 16-byte chunks per row, NK = D / 16 16-deep k steps
+// over the head dimension and ND = D / 32 32-wide head-dimension blocks of an
+// accumulator.
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------- delta --
-constexpr int DELTA_ROWS = 16;  // 16 lanes per row, 8 head dims each
+constexpr int DELTA_ROWS = 16;  // 16 lanes per row, 8 head dims each (lanes past D idle)
 
+template <int D>
 __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int sub = tid & 15;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
   float acc = 0.f;
-  if (t < p.N) {
+  if (t < p.N && 8 * sub < D) {
     const u32x4 dw = ldg16(p.dout + (int64_t)b * p.dos_b + (int64_t)t * p.dos_t +
                            (int64_t)hq * p.dos_h + 8 * sub);
     const int64_t oi = (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)hq * p.os_h + 8 * sub;
@@ -97,16 +98,18 @@ __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   }
 }
 
-// Offsets of the plain 16-byte reads of a swizzled [rows x 128] tile feeding
+// Offsets of the plain 16-byte reads of a swizzled [rows x D] tile feeding
 // an A operand: row 32 blk + (lane % 32), chunk 2 ks + lane / 32.
-__device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][NK]) {
+template <int D>
+__device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][D / 16]) {
+  constexpr int NK = D / 16;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       // rows l32 and 32 + l32 share the swizzle: the two blocks differ by a
       // constant, which the compiler folds into the read's offset field
-      off[blk][ks] = 32 * blk * D + l32 * D + (((2 * ks + hl) ^ swz_both_d128(l32)) * 8);
+      off[blk][ks] = 32 * blk * D + l32 * D + (((2 * ks + hl) ^ swz_both<D>(l32)) * 8);
     }
 }
 
@@ -114,7 +117,9 @@ __device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][NK]
 // over 16 tile rows (add 16 D per step): half ri, head-dim block db; lane
 // addresses row 8 ri + 4 (lane / 32) + (lane % 16) / 4 at dims
 // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3.
-__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][ND]) {
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
+  constexpr int ND = D / 32;
   const int hl = lane >> 5, r16 = lane & 15, gi = (lane >> 4) & 1;
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri)
@@ -122,7 +127,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][ND]) {
     for (int db = 0; db < ND; ++db) {
       const int row = 8 * ri + 4 * hl + (r16 >> 2);
       const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
-      off[ri][db] = row * D + (((d >> 3) ^ swz_both_d128(row)) * 8) + (d & 7);
+      off[ri][db] = row * D + (((d >> 3) ^ swz_both<D>(row)) * 8) + (d & 7);
     }
 }
 
@@ -171,9 +176,10 @@ constexpr int QBN = kFwdBlockN;  // 64 keys per tile
 constexpr int QWAVES = QBM / 32;
 constexpr int QTHREADS = 64 * QWAVES;
 
-template <bool GF32>
+template <int D, bool GF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void cowa_bwd_dq_kernel(BwdParams p) {
+  constexpr int CPR = D / 8, NK = D / 16, ND = D / 32;
   constexpr int TILE = QBN * D;
   constexpr int LOADS = QBN * CPR / 64 / QWAVES;
   static_assert(LOADS >= 1, "every wavefront loads part of each tile");
@@ -238,7 +244,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
-    ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
+    ld_col[i] = ((P % CPR) ^ swz_both<D>(ld_row[i])) * 8;
     ld_koff[i] = (uint32_t)(ld_row[i] * p.ks_t) + ld_col[i];
     ld_voff[i] = (uint32_t)(ld_row[i] * p.vs_t) + ld_col[i];
   }
@@ -266,8 +272,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   };
 
   int n_off[2][NK], t_off[2][ND];
-  plain_offsets(l32, hl, n_off);
-  tr_offsets(lane, t_off);
+  plain_offsets<D>(l32, hl, n_off);
+  tr_offsets<D>(lane, t_off);
 
   PlanCursor pc;
   pc.init(p.col, p.flags, e0, e1, lane);
@@ -377,9 +383,10 @@ constexpr int KBN = kBwdBlockN;  // 128 keys per workgroup
 constexpr int KWAVES = KBN / 32;
 constexpr int KTHREADS = 64 * KWAVES;
 
-template <bool GF32>
+template <int D, bool GF32>
 __device__ __forceinline__ void store_key_row(void* base, int64_t idx, const f32x16* acc,
                                               float mul, int hl) {
+  constexpr int ND = D / 32;
   char* g = reinterpret_cast<char*>(base);
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -396,9 +403,10 @@ __device__ __forceinline__ void store_key_row(void* base, int64_t idx, const f32
     }
 }
 
-template <bool GF32>
+template <int D, bool GF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
                           amdgpu_waves_per_eu(1, 1))) void cowa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int CPR = D / 8, NK = D / 16, ND = D / 32;
   constexpr int TILE = KBM * D;
   constexpr int LOADS = KBM * CPR / 64 / KWAVES;
   static_assert(LOADS >= 1, "every wavefront loads part of each tile");
@@ -489,7 +497,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   for (int i = 0; i < LOADS; ++i) {
     const int P = (wave * LOADS + i) * 64 + lane;
     ld_row[i] = P / CPR;
-    ld_col[i] = ((P % CPR) ^ swz_both_d128(ld_row[i])) * 8;
+    ld_col[i] = ((P % CPR) ^ swz_both<D>(ld_row[i])) * 8;
     ld_qoff[i] = (uint32_t)(ld_row[i] * p.qs_t) + ld_col[i];
     ld_ooff[i] = (uint32_t)(ld_row[i] * p.dos_t) + ld_col[i];
   }
@@ -522,8 +530,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   };
 
   int n_off[2][NK], t_off[2][ND];
-  plain_offsets(l32, hl, n_off);
-  tr_offsets(lane, t_off);
+  plain_offsets<D>(l32, hl, n_off);
+  tr_offsets<D>(lane, t_off);
 
   int hq_cur = h * p.G, e_cur = e0, c_cur = 0;
   if (cnt > 0) {
@@ -641,31 +649,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     const int64_t slot =
         (((int64_t)(b * p.Hkv + h) * p.n_sink_tiles + kj) * p.nch + part) * 2;
     const int64_t row = (int64_t)(wave * 32 + l32) * D;
-    store_key_row<true>(p.part, slot * KBN * D + row, dk, p.scale, hl);
-    store_key_row<true>(p.part, (slot + 1) * KBN * D + row, dv, 1.f, hl);
+    store_key_row<D, true>(p.part, slot * KBN * D + row, dk, p.scale, hl);
+    store_key_row<D, true>(p.part, (slot + 1) * KBN * D + row, dv, 1.f, hl);
   } else if (key < p.N) {
-    store_key_row<GF32>(p.dk,
+    store_key_row<D, GF32>(p.dk,
                         (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h, dk,
                         p.scale, hl);
-    store_key_row<GF32>(p.dv,
+    store_key_row<D, GF32>(p.dv,
                         (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h, dv,
                         1.f, hl);
   }
 }
 
 // Sum of the parts of the split sink key tiles, in part order.  Grid
-// (H_kv * n_sink_tiles * REDUCE_SPLIT, B); each workgroup covers 16 keys,
-// each thread 8 head dims of one key.
-constexpr int REDUCE_SPLIT = KBN / 16;
-template <bool GF32>
+// (H_kv * n_sink_tiles * reduce_split(D), B); each thread covers 8 head dims
+// of one key, each workgroup 256 / (D / 8) keys.
+constexpr int reduce_split(int d) { return KBN * (d / 8) / 256; }
+template <int D, bool GF32>
 __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) {
+  constexpr int REDUCE_SPLIT = reduce_split(D);
   const int t = blockIdx.x / REDUCE_SPLIT;
   const int kj = t % p.n_sink_tiles;
   const int h = t / p.n_sink_tiles;
   const int b = blockIdx.y;
   const int64_t slot0 = (((int64_t)(b * p.Hkv + h) * p.n_sink_tiles + kj) * p.nch) * 2;
   {
-    const int u = (blockIdx.x % REDUCE_SPLIT) * 256 + threadIdx.x;  // 16 keys x 16 chunks
+    const int u = (blockIdx.x % REDUCE_SPLIT) * 256 + threadIdx.x;  // key x (D / 8) chunks
     const int kl = u / (D / 8);
     const int d0 = (u % (D / 8)) * 8;
     const int key = kj * KBN + kl;
@@ -694,34 +703,40 @@ __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) 
   }
 }
 
-}  // namespace
-
-int launch_bwd(const BwdParams& p_in, int d, void* stream) {
-  if (d != D) return (int)hipErrorInvalidValue;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+template <int D>
+int launch_bwd_d(const BwdParams& p_in, hipStream_t s) {
   // XCD chunks: up to 8 query tiles with all their heads (dQ); up to
   // KV_CHUNK_TILES key tiles with all their (sequence, head) pairs (dK/dV)
   BwdParams p = p_in;
   const int64_t kv_units = p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1);
   p.xcd_chunk_q = xcd_chunk(p.Hq, (int64_t)p.B * p.nqt, 8);
   p.xcd_chunk_kv = xcd_chunk((int64_t)p.B * p.Hkv, kv_units, KV_CHUNK_TILES);
-  hipLaunchKernelGGL(cowa_bwd_delta_kernel, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
+  hipLaunchKernelGGL(cowa_bwd_delta_kernel<D>, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
                      dim3(256), 0, s, p);
   const dim3 gq((unsigned)xcd_grid((int64_t)p.B * p.nqt * p.Hq, p.xcd_chunk_q));
   const dim3 gk((unsigned)xcd_grid((int64_t)p.B * p.Hkv * kv_units, p.xcd_chunk_kv));
-  const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles * REDUCE_SPLIT), (unsigned)p.B);
+  const dim3 gr((unsigned)(p.Hkv * p.n_sink_tiles * reduce_split(D)), (unsigned)p.B);
   if (p.g_f32) {
-    hipLaunchKernelGGL(cowa_bwd_dq_kernel<true>, gq, dim3(QTHREADS), 0, s, p);
-    hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<true>, gk, dim3(KTHREADS), 0, s, p);
+    hipLaunchKernelGGL((cowa_bwd_dq_kernel<D, true>), gq, dim3(QTHREADS), 0, s, p);
+    hipLaunchKernelGGL((cowa_bwd_dkdv_kernel<D, true>), gk, dim3(KTHREADS), 0, s, p);
     if (p.n_sink_tiles > 0)
-      hipLaunchKernelGGL(cowa_bwd_part_reduce_kernel<true>, gr, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((cowa_bwd_part_reduce_kernel<D, true>), gr, dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL(cowa_bwd_dq_kernel<false>, gq, dim3(QTHREADS), 0, s, p);
-    hipLaunchKernelGGL(cowa_bwd_dkdv_kernel<false>, gk, dim3(KTHREADS), 0, s, p);
+    hipLaunchKernelGGL((cowa_bwd_dq_kernel<D, false>), gq, dim3(QTHREADS), 0, s, p);
+    hipLaunchKernelGGL((cowa_bwd_dkdv_kernel<D, false>), gk, dim3(KTHREADS), 0, s, p);
     if (p.n_sink_tiles > 0)
-      hipLaunchKernelGGL(cowa_bwd_part_reduce_kernel<false>, gr, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((cowa_bwd_part_reduce_kernel<D, false>), gr, dim3(256), 0, s, p);
   }
   return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_bwd(const BwdParams& p, int d, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 128) return launch_bwd_d<128>(p, s);
+  if (d == 64) return launch_bwd_d<64>(p, s);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace cowa

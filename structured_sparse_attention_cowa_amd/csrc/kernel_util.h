@@ -105,5 +105,14 @@ __device__ __forceinline__ int swz_both_d128(int row) {
   return (((a << 2) ^ (a << 1)) & 14) ^ ((row >> 2) & 3);
 }
 
+// The same swizzle for [rows x D] tiles: for D = 64 (8 chunks per row) its low
+// three bits keep both read patterns free of bank conflicts (checked on the
+// host against a model of 128- and 256-byte LDS cycles).
+template <int D>
+__device__ __forceinline__ int swz_both(int row) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  return swz_both_d128(row) & (D / 8 - 1);
+}
+
 }  // namespace kern
 }  // namespace cowa

@@ -63,10 +63,10 @@ def test_plan_kv_8k_workload(lib):
 
 
 def test_bwd_block_sizes_and_workspace(lib):
-    bm, bn = C.cowa_bwd_block_sizes(128)
-    assert (bm, bn) == (64, 128)
+    for d in (64, 128):
+        assert C.cowa_bwd_block_sizes(d) == (64, 128)
     with pytest.raises(C.CowaError) as e:
-        C.cowa_bwd_block_sizes(64)
+        C.cowa_bwd_block_sizes(96)
     assert e.value.status == C.COWA_ERR_UNSUPPORTED
     # two fp32 arrays [B, H_q, N rounded up to 64], each 256-byte aligned, when
     # no key tile's step list is split
@@ -127,7 +127,7 @@ def test_bwd_host_validation(lib):
     assert _bwd_raw(lib, cp, nnz_kv=1) == E.COWA_ERR_PLAN_MISMATCH
     assert _bwd_raw(lib, cp, bm=128) == E.COWA_ERR_UNSUPPORTED
     assert _bwd_raw(lib, cp, bn_kv=64) == E.COWA_ERR_UNSUPPORTED
-    assert _bwd_raw(lib, cp, d=64) == E.COWA_ERR_UNSUPPORTED
+    assert _bwd_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
     assert _bwd_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
     # empty inputs are rejected before anything runs
     assert _bwd_raw(lib, cp, B=0, nnz=0, nnz_kv=0) == E.COWA_ERR_INVALID_ARG

@@ -82,6 +82,35 @@ def test_bwd_after_gpu_forward(lib, o_dtype, g_dtype):
           what=f"e2e o={o_dtype}")
 
 
+@pytest.mark.parametrize("gpu_forward,g_dtype", [(False, "f32"), (True, "bf16")])
+def test_bwd_tiny_workload_d64(lib, gpu_forward, g_dtype):
+    # the tiny workload itself (d = 64, its pattern), every gradient element
+    w = W.TINY
+    x = W.prefill_inputs(w)
+    _full(x, w.sink, w.window, w.h_kv_global, g_dtype=g_dtype, gpu_forward=gpu_forward,
+          what=f"tiny-d64 gpu_forward={gpu_forward}")
+
+
+@pytest.mark.parametrize("N,S,Wd,H,off,Hq,Hkv", [
+    (17, 2, 4, 4, 0, 8, 4),       # ragged, shorter than one tile
+    (129, 0, 1, 8, 3, 4, 2),      # band only, ragged key tile
+    (1000, 16, 128, 4, 1, 10, 2), # GQA 5, ragged
+])
+def test_bwd_edge_shapes_d64(lib, N, S, Wd, H, off, Hq, Hkv):
+    x = W.random_prefill(400 + N, 2, N, Hq, Hkv, 64)
+    _full(x, S, Wd, H, off, what=f"d64 N={N}")
+
+
+def test_bwd_split_sink_tiles_d64(lib):
+    # 100 query tiles x 4 heads see the sink key tile: its step list is cut into
+    # parts whose fp32 partials are summed by the reduction kernel
+    x = W.random_prefill(411, 1, 6400, 4, 1, 64)
+    from structured_sparse_attention_cowa_amd import binding as C
+    cp = C.make_pattern(6400, 32, 64, 0, 8, 0)
+    assert C.cowa_bwd_workspace_size(cp, 1, 4, 1, 6400) > 2 * (4 * 6400 * 4)
+    _full(x, 32, 64, 8, what="d64 split sink tiles")
+
+
 def test_bwd_2k_full(lib):
     x = W.random_prefill(205, 1, 2048, 6, 2, 128)
     _full(x, 64, 256, 8, off=5, what="2k")
