@@ -315,18 +315,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
         dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dof[ks], dpv, 0, 0, 0);
       }
       if (!full) {
-        // register i holds key kj*64 + 32 blk + 8 (i/4) + 4 hl + i%4
-        const int dist0 = q_row - (kj * QBN + 4 * hl);
-        const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
-        const int sink_rel = hp.sink - (kj * QBN + 4 * hl);
+        // register i holds key kj*64 + 4 hl + 32 blk + 8 (i/4) + i%4
+        const uint64_t vis = row_visible_bits(hp, q_row, kj * QBN + 4 * hl);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int o = 32 * blk + 8 * (i >> 2) + (i & 3);
-          const int dist = dist0 - o;
-          const bool win = (o < sink_rel) | (dist < hp.window) |
-                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
-          s[i] = ((dist >= 0) & win) ? s[i] : NEG_INF;
-        }
+        for (int i = 0; i < 16; ++i) s[i] = keep_if(s[i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -550,8 +542,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
-  const bool key_sink = key < hp.sink;
   // One step on the tiles in (Qs, Os, Ss) while the next ones stream into
   // (Qn, On, Sn).
   auto step = [&](int s, const uint16_t* Qs, const uint16_t* Os, const float* Ss, uint16_t* Qn,
@@ -585,15 +575,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
         dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dpv, 0, 0, 0);
       }
       if (!full) {
-        // register i holds query qi*64 + 32 blk + 8 (i/4) + 4 hl + i%4
-        const int dist0 = qi * KBM + 4 * hl - key;
+        // register i holds query qi*64 + 4 hl + 32 blk + 8 (i/4) + i%4
+        const uint64_t vis = col_visible_bits(hp, qi * KBM + 4 * hl, key);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dist = dist0 + 32 * blk + 8 * (i >> 2) + (i & 3);
-          const bool win = key_sink | (dist < hp.window) |
-                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
-          sv[i] = ((dist >= 0) & win) ? sv[i] : NEG_INF;
-        }
+        for (int i = 0; i < 16; ++i)
+          sv[i] = keep_if(sv[i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

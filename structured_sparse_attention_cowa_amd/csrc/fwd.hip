@@ -266,20 +266,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     if (has_next) load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_n1 & 0x7fffffff, Vw);
 
     if (!full) {
-      // branch-free form of the visibility predicate vis_g(t, j)
-      const int dist0 = q_row - (kj * BN + 4 * hl);
-      const unsigned band_len = (unsigned)(hp.band_hi - hp.band_lo);
-      const int sink_rel = hp.sink - (kj * BN + 4 * hl);
+      // register i of block blk holds key kj*64 + 4 hl + o
+      const uint64_t vis = row_visible_bits(hp, q_row, kj * BN + 4 * hl);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int o = 32 * blk + 8 * (i >> 2) + (i & 3);
-          const int dist = dist0 - o;
-          const bool win = (o < sink_rel) | (dist < hp.window) |
-                           ((unsigned)(dist - hp.band_lo) < band_len) | (hp.causal != 0);
-          s_cur[blk][i] = ((dist >= 0) & win) ? s_cur[blk][i] : NEG_INF;
-        }
+        for (int i = 0; i < 16; ++i)
+          s_cur[blk][i] = keep_if(s_cur[blk][i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
     }
 
     float mt = NEG_INF;

@@ -43,6 +43,47 @@ __device__ __forceinline__ int xcd_logical(int i, int chunk, int total) {
   return l < total ? l : -1;
 }
 
+// Masking of partial tiles.  Within a tile, the keys (or queries) a lane
+// sees form at most three intervals of the element offset o in [0, 64): the
+// sink, the local window and the band of vis_g(t, j) (cowa_pattern.h).  Each
+// lane folds them into one 64-bit mask; an element is then kept or set to
+// -inf with a sign-extended bit extract and a bitfield insert.
+
+// Bits [lo, hi) of a 64-bit mask, with lo and hi clamped to [0, 64].
+__device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
+  lo = min(max(lo, 0), 64);
+  hi = min(max(hi, lo), 64);
+  const int w = hi - lo;  // lo <= 63 whenever w > 0
+  return w == 0 ? 0ull : (((2ull << (w - 1)) - 1ull) << lo);
+}
+
+// Row form: the lane is query t, element o is key j = base + o.
+__device__ __forceinline__ uint64_t row_visible_bits(const HeadPattern& hp, int t, int base) {
+  const int d0 = t - base;  // o <= d0 is j <= t
+  if (hp.causal) return bit_range(0, d0 + 1);
+  // a window longer than d0 + 65 covers the same offsets (and keeps d0 - w in
+  // range); the band lies at distances >= W >= 1, so it is causal by itself
+  const int w = min(hp.window, max(d0, 0) + 65);
+  return bit_range(0, min(hp.sink - base, d0 + 1)) | bit_range(d0 - w + 1, d0 + 1) |
+         bit_range(d0 - hp.band_hi + 1, d0 - hp.band_lo + 1);
+}
+
+// Column form: the lane is key j, element o is query t = base + o.
+__device__ __forceinline__ uint64_t col_visible_bits(const HeadPattern& hp, int base, int j) {
+  const int c0 = j - base;  // o >= c0 is t >= j
+  if (hp.causal || j < hp.sink) return bit_range(c0, 64);
+  // offsets past 63 do not matter: the window is cut to 64 - c0 (no overflow)
+  const int w = min(hp.window, 64 - c0);
+  return bit_range(c0, c0 + w) | bit_range(c0 + hp.band_lo, c0 + hp.band_hi);
+}
+
+// s if bit o of m is set, else -inf (o is a compile-time constant).
+__device__ __forceinline__ float keep_if(float s, uint64_t m, int o) {
+  const int word = (int)(o < 32 ? (uint32_t)m : (uint32_t)(m >> 32));
+  const unsigned keep = (unsigned)__builtin_amdgcn_sbfe(word, o & 31, 1);
+  return __uint_as_float((__float_as_uint(s) & keep) | (0xff800000u & ~keep));
+}
+
 // Lane l and lane l^32 hold the two halves of one accumulator column; this
 // returns (value of lane l, value of lane l^32) in some order on every lane.
 __device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
