@@ -292,6 +292,39 @@ cowa_status cowa_bwd(const cowa_pattern* p,
                      const int64_t strides[24], float softmax_scale,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Backward of the packed (varlen) prefill (cowa_fwd_varlen): the gradients of
+ * n_seqs sequences of different lengths in one call, training on packed
+ * batches with the same operator ("CoWindow Attention: Full Causal Coverage Is
+ * a Collective Property", Abstract: one pattern in training and inference).
+ * Sequence b is at token rows [cu_seqlens[b], cu_seqlens[b+1]) of q, o, dout,
+ * dq [total_tokens, H_q, d] and k, v, dk, dv [total_tokens, H_kv_local, d];
+ * positions restart at 0 in every sequence, and no sequence sees another's
+ * tokens.
+ *  cu_seqlens     device int32[n_seqs + 1], as in cowa_fwd_varlen (lengths
+ *                 <= max_seqlen are not checked on the host: rows past
+ *                 max_seqlen get no gradient)
+ *  plans          cowa_plan and cowa_plan_kv for n = max_seqlen (one pair serves
+ *                 every length)
+ *  lse            forward LSE fp32 [H_q, total_tokens] (cowa_fwd_varlen's)
+ *  strides        element strides (t, h) of q, k, v, o, dout, dq, dk, dv (16)
+ *  workspace      cowa_bwd_workspace_size(p, n_seqs, H_q, H_kv_local,
+ *                 max_seqlen) bytes, 256-byte aligned
+ * Everything else, errors included, as in cowa_bwd; n_seqs, max_seqlen and
+ * total_tokens must be >= 1 (COWA_ERR_INVALID_ARG otherwise). */
+cowa_status cowa_bwd_varlen(const cowa_pattern* p,
+                            const int32_t* d_row_ptr, const int32_t* d_col,
+                            const uint8_t* d_flags, int64_t nnz, int32_t block_m,
+                            int32_t block_n, const int32_t* d_row_ptr_kv,
+                            const int32_t* d_col_kv, const uint8_t* d_flags_kv,
+                            int64_t nnz_kv, int32_t block_m_kv, int32_t block_n_kv,
+                            const void* q, const void* k, const void* v, const void* o,
+                            int32_t o_dtype, const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv, int32_t g_dtype,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
+                            int32_t total_tokens, int32_t H_q, int32_t H_kv_local, int32_t d,
+                            const int64_t strides[16], float softmax_scale,
+                            void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

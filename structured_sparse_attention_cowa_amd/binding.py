@@ -32,7 +32,7 @@ COWA_DTYPE_F32 = 1
 EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa_plan_size",
             "cowa_plan", "cowa_fwd", "cowa_decode_workspace_size", "cowa_decode",
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
-            "cowa_bwd_workspace_size", "cowa_bwd", "cowa_kv_window_rows",
+            "cowa_bwd_workspace_size", "cowa_bwd", "cowa_bwd_varlen", "cowa_kv_window_rows",
             "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window",
             "cowa_fwd_varlen")
 
@@ -105,6 +105,11 @@ def load():
     lib.cowa_bwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, i32, i32,
                              vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
                              i32, i32, i32, i32, i32, P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_bwd_varlen.restype = ctypes.c_int
+    lib.cowa_bwd_varlen.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, i32, i32,
+                                    vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
+                                    vp, i32, i32, i32, i32, i32, i32, P(i64), f32, vp,
+                                    ctypes.c_size_t, vp]
     lib.cowa_kv_window_rows.restype = ctypes.c_int
     lib.cowa_kv_window_rows.argtypes = [pat, i32, i32, vp, P(i64)]
     lib.cowa_kv_window_fill.restype = ctypes.c_int
@@ -322,6 +327,48 @@ def cowa_bwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block
                          float(softmax_scale), workspace.data_ptr(),
                          workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check(st, "cowa_bwd")
+
+
+def cowa_bwd_varlen(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
+                    row_ptr_kv, col_kv, flags_kv, nnz_kv: int, block_m_kv: int,
+                    block_n_kv: int, q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens,
+                    max_seqlen: int, softmax_scale: float, workspace, stream=None):
+    """Packed backward: q/o/dout/dq [T, H_q, d], k/v/dk/dv [T, H_kv, d], lse [H_q, T]
+    (cowa_fwd_varlen's), cu_seqlens int32 [n_seqs + 1] on the device; both plans
+    are built for n = max_seqlen."""
+    import torch
+    for t in (q, k, v, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v, dout must be bfloat16 GPU tensors")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise TypeError("cu_seqlens must be an int32 GPU tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk, dv must share one dtype")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    for t in (k, v, dk, dv):
+        if tuple(t.shape) != (T, Hkv, d):
+            raise ValueError("k, v, dk, dv must be [T, H_kv, d]")
+    for t in (o, dout, dq):
+        if tuple(t.shape) != (T, Hq, d):
+            raise ValueError("o, dout, dq must be [T, H_q, d]")
+    if tuple(lse.shape) != (Hq, T):
+        raise ValueError("lse must be [H_q, T]")
+    strides = (ctypes.c_int64 * 16)(*(sum((_strides(t, 2) for t in (q, k, v, o, dout, dq, dk,
+                                                                       dv)), [])))
+    st = load().cowa_bwd_varlen(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(),
+                                flags.data_ptr(), nnz, block_m, block_n, row_ptr_kv.data_ptr(),
+                                col_kv.data_ptr(), flags_kv.data_ptr(), nnz_kv, block_m_kv,
+                                block_n_kv, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                o.data_ptr(), _o_dtype(o), dout.data_ptr(), lse.data_ptr(),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _o_dtype(dq),
+                                cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, max_seqlen, T, Hq,
+                                Hkv, d, strides, float(softmax_scale), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(),
+                                _stream_ptr(stream))
+    _check(st, "cowa_bwd_varlen")
 
 
 def cowa_kv_window_rows(p: cowa_pattern, h_kv_local: int, n_max: int):

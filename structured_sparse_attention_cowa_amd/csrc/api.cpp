@@ -470,17 +470,19 @@ extern "C" cowa_status cowa_bwd_workspace_size(const cowa_pattern* p, int32_t B,
   return COWA_OK;
 }
 
-extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
-                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
-                                int32_t block_m, int32_t block_n, const int32_t* d_row_ptr_kv,
-                                const int32_t* d_col_kv, const uint8_t* d_flags_kv,
-                                int64_t nnz_kv, int32_t block_m_kv, int32_t block_n_kv,
-                                const void* q, const void* k, const void* v, const void* o,
-                                int32_t o_dtype, const void* dout, const float* lse, void* dq,
-                                void* dk, void* dv, int32_t g_dtype, int32_t B, int32_t N,
-                                int32_t H_q, int32_t H_kv_local, int32_t d,
-                                const int64_t strides[24], float softmax_scale, void* workspace,
-                                size_t ws_bytes, void* stream) {
+// The backward for the batched layout (cu_seqlens NULL) or for packed
+// sequences (B = n_seqs, N = max_seqlen, b strides 0).
+static cowa_status bwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr,
+                            const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                            int32_t block_m, int32_t block_n, const int32_t* d_row_ptr_kv,
+                            const int32_t* d_col_kv, const uint8_t* d_flags_kv, int64_t nnz_kv,
+                            int32_t block_m_kv, int32_t block_n_kv, const void* q, const void* k,
+                            const void* v, const void* o, int32_t o_dtype, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int32_t g_dtype,
+                            int32_t B, int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
+                            const int64_t strides[24], float softmax_scale, void* workspace,
+                            size_t ws_bytes, void* stream, const int32_t* cu_seqlens,
+                            int32_t total_tokens) {
   cowa_status st = validate_pattern(p, H_kv_local);
   if (st != COWA_OK) return st;
   if (!d_row_ptr || !d_col || !d_flags || !d_row_ptr_kv || !d_col_kv || !d_flags_kv || !q ||
@@ -567,5 +569,50 @@ extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
   bp.g_f32 = g_dtype == COWA_DTYPE_F32;
   bp.scale = softmax_scale;
   bp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  bp.cu_seqlens = cu_seqlens;
+  bp.total_tokens = total_tokens;
   return launch_bwd(bp, d, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_bwd(const cowa_pattern* p, const int32_t* d_row_ptr,
+                                const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
+                                int32_t block_m, int32_t block_n, const int32_t* d_row_ptr_kv,
+                                const int32_t* d_col_kv, const uint8_t* d_flags_kv,
+                                int64_t nnz_kv, int32_t block_m_kv, int32_t block_n_kv,
+                                const void* q, const void* k, const void* v, const void* o,
+                                int32_t o_dtype, const void* dout, const float* lse, void* dq,
+                                void* dk, void* dv, int32_t g_dtype, int32_t B, int32_t N,
+                                int32_t H_q, int32_t H_kv_local, int32_t d,
+                                const int64_t strides[24], float softmax_scale, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  return bwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, d_row_ptr_kv, d_col_kv,
+                  d_flags_kv, nnz_kv, block_m_kv, block_n_kv, q, k, v, o, o_dtype, dout, lse, dq,
+                  dk, dv, g_dtype, B, N, H_q, H_kv_local, d, strides, softmax_scale, workspace,
+                  ws_bytes, stream, nullptr, 0);
+}
+
+extern "C" cowa_status cowa_bwd_varlen(
+    const cowa_pattern* p, const int32_t* d_row_ptr, const int32_t* d_col,
+    const uint8_t* d_flags, int64_t nnz, int32_t block_m, int32_t block_n,
+    const int32_t* d_row_ptr_kv, const int32_t* d_col_kv, const uint8_t* d_flags_kv,
+    int64_t nnz_kv, int32_t block_m_kv, int32_t block_n_kv, const void* q, const void* k,
+    const void* v, const void* o, int32_t o_dtype, const void* dout, const float* lse, void* dq,
+    void* dk, void* dv, int32_t g_dtype, const int32_t* cu_seqlens, int32_t n_seqs,
+    int32_t max_seqlen, int32_t total_tokens, int32_t H_q, int32_t H_kv_local, int32_t d,
+    const int64_t strides[16], float softmax_scale, void* workspace, size_t ws_bytes,
+    void* stream) {
+  if (!cu_seqlens || !strides) return COWA_ERR_INVALID_ARG;
+  if (n_seqs < 1 || total_tokens < 1 || max_seqlen < 1) return COWA_ERR_INVALID_ARG;
+  // token rows: (t, h) strides of q, k, v, o, dout, dq, dk, dv; the per-sequence
+  // offset comes from cu_seqlens
+  int64_t full[24];
+  for (int i = 0; i < 8; ++i) {
+    full[3 * i] = 0;
+    full[3 * i + 1] = strides[2 * i];
+    full[3 * i + 2] = strides[2 * i + 1];
+  }
+  return bwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, d_row_ptr_kv, d_col_kv,
+                  d_flags_kv, nnz_kv, block_m_kv, block_n_kv, q, k, v, o, o_dtype, dout, lse, dq,
+                  dk, dv, g_dtype, n_seqs, max_seqlen, H_q, H_kv_local, d, full, softmax_scale,
+                  workspace, ws_bytes, stream, cu_seqlens, total_tokens);
 }

@@ -55,6 +55,19 @@ using namespace kern;
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Sequence b: its first token row and its length.  Packed sequences take
+// both from cu_seqlens (the b strides are 0); the batched layout has row 0
+// and length N (its b strides select the sequence).  A negative length is an
+// empty sequence.
+struct SeqSpan {
+  int start, n;
+};
+__device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
+  if (!p.cu_seqlens) return {0, p.N};
+  const int s = p.cu_seqlens[b];
+  return {s, min(p.cu_seqlens[b + 1] - s, p.N)};
+}
+
 // ---------------------------------------------------------------- delta --
 constexpr int DELTA_ROWS = 16;  // 16 lanes per row, 8 head dims each (lanes past D idle)
 
@@ -65,11 +78,13 @@ __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   const int t = blockIdx.x * DELTA_ROWS + (tid >> 4);
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
+  const SeqSpan sp = seq_span(p, b);
+  const int64_t row = (int64_t)sp.start + t;  // token row of position t
   float acc = 0.f;
-  if (t < p.N && 8 * sub < D) {
-    const u32x4 dw = ldg16(p.dout + (int64_t)b * p.dos_b + (int64_t)t * p.dos_t +
+  if (t < sp.n && 8 * sub < D) {
+    const u32x4 dw = ldg16(p.dout + (int64_t)b * p.dos_b + row * p.dos_t +
                            (int64_t)hq * p.dos_h + 8 * sub);
-    const int64_t oi = (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)hq * p.os_h + 8 * sub;
+    const int64_t oi = (int64_t)b * p.os_b + row * p.os_t + (int64_t)hq * p.os_h + 8 * sub;
     float o[8];
     if (p.o_f32) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + oi);
@@ -93,8 +108,9 @@ __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   acc += __shfl_xor(acc, 8);
   if (sub == 0 && t < p.npad) {
     const int64_t bh = (int64_t)b * p.Hq + hq;
-    p.delta[bh * p.npad + t] = t < p.N ? acc : 0.f;
-    p.lse2[bh * p.npad + t] = t < p.N ? p.lse[bh * p.N + t] * LOG2E : POS_INF;
+    const int64_t li = p.cu_seqlens ? (int64_t)hq * p.total_tokens + row : bh * p.N + t;
+    p.delta[bh * p.npad + t] = t < sp.n ? acc : 0.f;
+    p.lse2[bh * p.npad + t] = t < sp.n ? p.lse[li] * LOG2E : POS_INF;
   }
 }
 
@@ -208,14 +224,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
                                       band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
+  const SeqSpan sp = seq_span(p, b);
+  if (qi * QBM >= sp.n) return;  // the whole workgroup: this tile is past the sequence
   const int q_row = qi * QBM + wave * 32 + l32;
-  const int q_row_c = q_row < p.N ? q_row : p.N - 1;
+  const int q_row_c = q_row < sp.n ? q_row : sp.n - 1;
   bf16x8 qf[NK], dof[NK];
   {
-    const uint16_t* qp =
-        p.q + (int64_t)b * p.qs_b + (int64_t)q_row_c * p.qs_t + (int64_t)hq * p.qs_h;
-    const uint16_t* dp =
-        p.dout + (int64_t)b * p.dos_b + (int64_t)q_row_c * p.dos_t + (int64_t)hq * p.dos_h;
+    const int64_t r = (int64_t)sp.start + q_row_c;
+    const uint16_t* qp = p.q + (int64_t)b * p.qs_b + r * p.qs_t + (int64_t)hq * p.qs_h;
+    const uint16_t* dp = p.dout + (int64_t)b * p.dos_b + r * p.dos_t + (int64_t)hq * p.dos_h;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks + 8 * hl));
@@ -233,8 +250,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const int row = h * p.nqt + qi;
   const int e0 = p.row_ptr[row];
   const int e1 = p.row_ptr[row + 1];
-  const uint16_t* kbase = p.k + (int64_t)b * p.ks_b + (int64_t)h * p.ks_h;
-  const uint16_t* vbase = p.v + (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+  const uint16_t* kbase =
+      p.k + (int64_t)b * p.ks_b + (int64_t)sp.start * p.ks_t + (int64_t)h * p.ks_h;
+  const uint16_t* vbase =
+      p.v + (int64_t)b * p.vs_b + (int64_t)sp.start * p.vs_t + (int64_t)h * p.vs_h;
 
   // lane offsets inside a tile are unsigned 32-bit (the host bounds 64 rows x
   // stride below 2^31), so the loads use a uniform 64-bit base plus a 32-bit offset
@@ -252,7 +271,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   // tiles the plan marks partial, where they are masked) are clamped.
   auto load_kv = [&](int kj, uint16_t* kd, uint16_t* vd) {
     const int key0 = kj * QBN;
-    if (key0 + QBN <= p.N) {
+    if (key0 + QBN <= sp.n) {
       const uint16_t* kt = kbase + (int64_t)key0 * p.ks_t;
       const uint16_t* vt = vbase + (int64_t)key0 * p.vs_t;
 #pragma unroll
@@ -264,7 +283,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
-        key = key < p.N ? key : p.N - 1;
+        key = key < sp.n ? key : sp.n - 1;
         g2lds16(kbase + (int64_t)key * p.ks_t + ld_col[i], kd + (wave * LOADS + i) * 512);
         g2lds16(vbase + (int64_t)key * p.vs_t + ld_col[i], vd + (wave * LOADS + i) * 512);
       }
@@ -350,9 +369,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
     if (e + 1 < e1) step(e + 1, K1, V1, K0, V0);
   }
 
-  if (q_row < p.N) {
+  if (q_row < sp.n) {
     char* gbase = reinterpret_cast<char*>(p.dq);
-    const int64_t gi = (int64_t)b * p.dqs_b + (int64_t)q_row * p.dqs_t + (int64_t)hq * p.dqs_h;
+    const int64_t gi = (int64_t)b * p.dqs_b + ((int64_t)sp.start + q_row) * p.dqs_t +
+                       (int64_t)hq * p.dqs_h;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -441,12 +461,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   const HeadPattern hp = head_pattern(p.sink, p.window, p.band,
                                       band_slot(p.kv_head_offset + h, p.n_bands), p.causal);
 
+  const SeqSpan sp = seq_span(p, b);
+  if (kj * KBN >= sp.n) return;  // the whole workgroup: this tile is past the sequence
   const int key = kj * KBN + wave * 32 + l32;
-  const int key_c = key < p.N ? key : p.N - 1;
+  const int key_c = key < sp.n ? key : sp.n - 1;
   bf16x8 kf[NK], vf[NK];
   {
-    const uint16_t* kp = p.k + (int64_t)b * p.ks_b + (int64_t)key_c * p.ks_t + (int64_t)h * p.ks_h;
-    const uint16_t* vp = p.v + (int64_t)b * p.vs_b + (int64_t)key_c * p.vs_t + (int64_t)h * p.vs_h;
+    const int64_t r = (int64_t)sp.start + key_c;
+    const uint16_t* kp = p.k + (int64_t)b * p.ks_b + r * p.ks_t + (int64_t)h * p.ks_h;
+    const uint16_t* vp = p.v + (int64_t)b * p.vs_b + r * p.vs_t + (int64_t)h * p.vs_h;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       kf[ks] = __builtin_bit_cast(bf16x8, ldg16(kp + 16 * ks + 8 * hl));
@@ -472,7 +495,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   // takes one contiguous range of them
   const int r = h * p.nkt_kv + kj;
   const int e0 = p.row_ptr_kv[r];
-  const int e1 = p.row_ptr_kv[r + 1];
+  int e1 = p.row_ptr_kv[r + 1];
+  if (p.cu_seqlens) {
+    // the plan is built for the longest sequence: keep the query tiles that
+    // start inside this one (the list is ascending)
+    const int nq = (sp.n + KBM - 1) / KBM;
+    int lo = e0, hi = e1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.col_kv[mid] < nq) lo = mid + 1;
+      else hi = mid;
+    }
+    e1 = lo;
+  }
   const int cnt = e1 - e0;
   const int total = cnt * p.G;
   int s_begin = 0, s_end = total;
@@ -497,9 +532,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
   // tile's LSE2 and D; rows past N are clamped (their LSE2 is +inf).
   auto load_q = [&](int hq, int qi, uint16_t* qd, uint16_t* od, float* sdst) {
     const int r0 = qi * KBM;
-    const uint16_t* qb = p.q + (int64_t)b * p.qs_b + (int64_t)hq * p.qs_h;
-    const uint16_t* ob = p.dout + (int64_t)b * p.dos_b + (int64_t)hq * p.dos_h;
-    if (r0 + KBM <= p.N) {
+    const uint16_t* qb =
+        p.q + (int64_t)b * p.qs_b + (int64_t)sp.start * p.qs_t + (int64_t)hq * p.qs_h;
+    const uint16_t* ob =
+        p.dout + (int64_t)b * p.dos_b + (int64_t)sp.start * p.dos_t + (int64_t)hq * p.dos_h;
+    if (r0 + KBM <= sp.n) {
       const uint16_t* qt = qb + (int64_t)r0 * p.qs_t;
       const uint16_t* ot = ob + (int64_t)r0 * p.dos_t;
 #pragma unroll
@@ -511,7 +548,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int t = r0 + ld_row[i];
-        t = t < p.N ? t : p.N - 1;
+        t = t < sp.n ? t : sp.n - 1;
         g2lds16(qb + (int64_t)t * p.qs_t + ld_col[i], qd + (wave * LOADS + i) * 512);
         g2lds16(ob + (int64_t)t * p.dos_t + ld_col[i], od + (wave * LOADS + i) * 512);
       }
@@ -637,13 +674,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
     const int64_t row = (int64_t)(wave * 32 + l32) * D;
     store_key_row<D, true>(p.part, slot * KBN * D + row, dk, p.scale, hl);
     store_key_row<D, true>(p.part, (slot + 1) * KBN * D + row, dv, 1.f, hl);
-  } else if (key < p.N) {
-    store_key_row<D, GF32>(p.dk,
-                        (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h, dk,
-                        p.scale, hl);
-    store_key_row<D, GF32>(p.dv,
-                        (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h, dv,
-                        1.f, hl);
+  } else if (key < sp.n) {
+    const int64_t row = (int64_t)sp.start + key;
+    store_key_row<D, GF32>(p.dk, (int64_t)b * p.dks_b + row * p.dks_t + (int64_t)h * p.dks_h,
+                           dk, p.scale, hl);
+    store_key_row<D, GF32>(p.dv, (int64_t)b * p.dvs_b + row * p.dvs_t + (int64_t)h * p.dvs_h,
+                           dv, 1.f, hl);
   }
 }
 
@@ -664,7 +700,9 @@ __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) 
     const int kl = u / (D / 8);
     const int d0 = (u % (D / 8)) * 8;
     const int key = kj * KBN + kl;
-    if (key >= p.N) return;
+    const SeqSpan sp = seq_span(p, b);
+    if (key >= sp.n) return;
+    const int64_t row = (int64_t)sp.start + key;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       f32x4 a = {}, c = {};
@@ -675,8 +713,8 @@ __global__ __launch_bounds__(256) void cowa_bwd_part_reduce_kernel(BwdParams p) 
       }
       void* dst = which == 0 ? p.dk : p.dv;
       const int64_t idx = which == 0
-          ? (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)h * p.dks_h + d0
-          : (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)h * p.dvs_h + d0;
+          ? (int64_t)b * p.dks_b + row * p.dks_t + (int64_t)h * p.dks_h + d0
+          : (int64_t)b * p.dvs_b + row * p.dvs_t + (int64_t)h * p.dvs_h + d0;
       if (GF32) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + idx) = a;
         *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + idx + 4) = c;

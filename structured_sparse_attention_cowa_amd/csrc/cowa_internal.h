@@ -143,6 +143,11 @@ struct BwdParams {
   int64_t dks_b, dks_t, dks_h;
   int64_t dvs_b, dvs_t, dvs_h;
   float* part;   // workspace: fp32 dK, dV partials of the split sink key tiles
+  // packed sequences (varlen): B sequences, sequence b at token rows
+  // [cu_seqlens[b], cu_seqlens[b+1]) of length <= N (b strides 0); LSE
+  // [H_q, total_tokens].  NULL: the batched layout.
+  const int32_t* cu_seqlens;
+  int32_t total_tokens;
   int32_t B, N, Hq, Hkv, G, nqt, nkt_kv, nqt_kv, npad;
   int32_t xcd_chunk_q, xcd_chunk_kv;  // workgroup chunks per XCD (set by launch_bwd)
   int32_t n_sink_tiles;  // leading key tiles whose step lists are split (0: none)

@@ -150,3 +150,50 @@ def test_bwd_host_validation(lib):
     other = C.cowa_plan_kv_size(cpw, 4096, 2, 64, 128)
     assert other != C.cowa_plan_kv_size(cp4, 4096, 2, 64, 128)
     assert _bwd_raw(lib, cp4, N=4096, nnz_kv=other) == E.COWA_ERR_PLAN_MISMATCH
+
+
+def _bwd_varlen_raw(lib, cp, lens=(100, 37), Hq=4, Hkv=2, d=128, nnz=None, nnz_kv=None,
+                    cu=0x2000, n_seqs=None, max_seqlen=None, total=None, ws_bytes=1 << 30,
+                    ws_ptr=0x100000):
+    """cowa_bwd_varlen with fake (never dereferenced) device pointers."""
+    max_seqlen = max(lens) if max_seqlen is None else max_seqlen
+    n_seqs = len(lens) if n_seqs is None else n_seqs
+    total = sum(lens) if total is None else total
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    kbm, kbn = C.cowa_bwd_block_sizes(128)
+    if nnz is None:
+        nnz = C.cowa_plan_size(cp, max(max_seqlen, 1), Hkv, fbm, fbn)
+    if nnz_kv is None:
+        nnz_kv = C.cowa_plan_kv_size(cp, max(max_seqlen, 1), Hkv, kbm, kbn)
+    fake = ctypes.c_void_p(0x1000)
+    arr = (ctypes.c_int64 * 16)(*([8] * 16))
+    return lib.cowa_bwd_varlen(ctypes.byref(cp), fake, fake, fake, nnz, fbm, fbn, fake, fake,
+                               fake, nnz_kv, kbm, kbn, fake, fake, fake, fake, 0, fake, fake,
+                               fake, fake, fake, 0, ctypes.c_void_p(cu) if cu else None, n_seqs,
+                               max_seqlen, total, Hq, Hkv, d, arr, 0.1,
+                               ctypes.c_void_p(ws_ptr), ws_bytes, None)
+
+
+def test_bwd_varlen_host_validation(lib):
+    cp, _ = pat(n_ctx=256, h_kv_global=2)
+    E = C
+    assert _bwd_varlen_raw(lib, cp, cu=0) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_varlen_raw(lib, cp, n_seqs=0) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_varlen_raw(lib, cp, max_seqlen=0) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_varlen_raw(lib, cp, total=0) == E.COWA_ERR_INVALID_ARG
+    assert _bwd_varlen_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
+    assert _bwd_varlen_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
+    # the plans must be the ones for n = max_seqlen
+    assert _bwd_varlen_raw(lib, cp, nnz=1) == E.COWA_ERR_PLAN_MISMATCH
+    assert _bwd_varlen_raw(lib, cp, nnz_kv=1) == E.COWA_ERR_PLAN_MISMATCH
+    # the workspace is sized for n_seqs sequences of max_seqlen rows
+    need = C.cowa_bwd_workspace_size(cp, 2, 4, 2, 100)
+    assert _bwd_varlen_raw(lib, cp, ws_bytes=need - 1) == E.COWA_ERR_WORKSPACE
+    assert _bwd_varlen_raw(lib, cp, ws_ptr=0x100010) == E.COWA_ERR_WORKSPACE
+
+
+def test_bwd_varlen_split_sink_tiles_in_workspace():
+    # the longest sequence (6400 rows, 4 heads) of the packed GPU test splits
+    # its sink key tile: the workspace then holds partials past LSE2 and D
+    cp = C.make_pattern(6400, 32, 64, 0, 8, 0)
+    assert C.cowa_bwd_workspace_size(cp, 3, 4, 1, 6400) > 2 * (3 * 4 * 6400 * 4)
