@@ -471,11 +471,32 @@ def varlen_prefill(C, W, torch, dev, time_it):
         pairs += sum(int(visible_counts(t, g, w.sink, w.window, band).sum())
                      for g in range(w.H_kv))
     flops = 4.0 * w.d * G * pairs
+    # the packed backward of the same batch (O and LSE from the forward above,
+    # dO N(0,1) drawn on the device; bf16 gradients): five products of the pairs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 1)
+    do = torch.randn((T, w.H_q, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    dq = torch.empty((T, w.H_q, w.d), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((T, w.H_kv, w.d), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((T, w.H_kv, w.d), dtype=torch.bfloat16, device=dev)
+    bmk, bnk = C.cowa_bwd_block_sizes(w.d)
+    rpk, colk, flk = [torch.from_numpy(a).to(dev)
+                      for a in C.cowa_plan_kv(p, max_len, w.H_kv, bmk, bnk)]
+    ws = torch.empty(C.cowa_bwd_workspace_size(p, len(lens), w.H_q, w.H_kv, max_len),
+                     dtype=torch.uint8, device=dev)
+    ms_b = time_it(lambda: C.cowa_bwd_varlen(p, rp, col, fl, col.numel(), bm, bn, rpk, colk, flk,
+                                             colk.numel(), bmk, bnk, q, k, v, o, do, lse, dq,
+                                             dk, dv, cu, max_len, 1.0 / np.sqrt(w.d), ws), 3)
+    flops_b = 2.5 * flops
     return {"workload": f"{w.n_seqs} packed sequences, lengths {[int(x) for x in lens]} "
                         f"({T} tokens), H_q=40, H_kv=8, d=128, S=128, W=4096, L={band}",
             "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "backward": {"ms": round(ms_b, 4), "tokens_per_s": round(T / (ms_b * 1e-3), 1),
+                         "tflops": round(flops_b / (ms_b * 1e-3) / 1e12, 1),
+                         "mfma_frac": round(flops_b / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                            4)}}
 
 
 def cpu_baseline(x, wp, scale, target_s=12.0):
