@@ -138,8 +138,9 @@ class Backward:
         self.rp_kv = torch.from_numpy(rp).cuda()
         self.col_kv = torch.from_numpy(col if len(col) else np.zeros(1, np.int32)).cuda()
         self.fl_kv = torch.from_numpy(fl if len(fl) else np.zeros(1, np.uint8)).cuda()
-        self.ws = torch.empty(C.cowa_bwd_workspace_size(pf.pattern, B, Hq, Hkv, N), dtype=torch.uint8,
-                              device="cuda")
+        # the workspace needs no initialisation: start it as NaN bytes
+        self.ws = torch.full((C.cowa_bwd_workspace_size(pf.pattern, B, Hq, Hkv, N),), 0xFF,
+                             dtype=torch.uint8, device="cuda")
         gdt = torch.float32 if g_dtype == "f32" else torch.bfloat16
         self.dq = torch.full((B, N, Hq, d), float("nan"), dtype=gdt, device="cuda")
         self.dk = torch.full((B, N, Hkv, d), float("nan"), dtype=gdt, device="cuda")

@@ -37,8 +37,8 @@ def _run(lens, Hq, Hkv, d, kw, seed, g_dtype):
     dq = torch.full((T, Hq, d), float("nan"), dtype=gdt, device="cuda")
     dk = torch.full((T, Hkv, d), float("nan"), dtype=gdt, device="cuda")
     dv = torch.full((T, Hkv, d), float("nan"), dtype=gdt, device="cuda")
-    ws = torch.empty(C.cowa_bwd_workspace_size(p, len(lens), Hq, Hkv, max_len),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.full((C.cowa_bwd_workspace_size(p, len(lens), Hq, Hkv, max_len),), 0xFF,
+                    dtype=torch.uint8, device="cuda")  # no initialisation needed
     cu_d = torch.from_numpy(cu).cuda()
     scale = 1.0 / np.sqrt(d)
     print(f"[bwd varlen] lens={list(lens)} Hq={Hq} Hkv={Hkv} d={d} {kw} g={g_dtype}", flush=True)

@@ -20,7 +20,8 @@ def run_decode(q_bits, k_dev, v_dev, lens, S, Wd, H, n_ctx, off=0, mode=0, o_dty
     n_max, Hkv = k_dev.shape[1], k_dev.shape[2]
     p = C.make_pattern(n_ctx, S, Wd, 0, H, off, mode)
     ws_bytes = C.cowa_decode_workspace_size(p, B, Hq, Hkv, d, n_max)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    # the workspace needs no initialisation: start it as NaN bytes
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
     q = bits_to_dev(q_bits)
     odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
     o = torch.full((B, Hq, d), float("nan"), dtype=odt, device="cuda")
