@@ -46,12 +46,27 @@ def visible_counts(t, g, sink, window, band):
     return n
 
 
+# headers every kernel source includes: a change to any of them, or to the
+# kernel source itself, invalidates the counters recorded for that kernel
+KERNEL_HEADERS = tuple(f"structured_sparse_attention_cowa_amd/csrc/{h}"
+                       for h in ("cowa_internal.h", "cowa_pattern.h", "kernel_util.h"))
+
+
+def source_digest(source: str) -> str:
+    """sha256 of the kernel source followed by KERNEL_HEADERS."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in (source,) + KERNEL_HEADERS:
+        h.update(open(os.path.join(ROOT, path), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(kernel: str, source: str):
     """Calibrated HBM bytes per launch from the committed rocprofv3 summaries
-    (profiles/*.md), or None when the kernel source changed since then."""
+    (profiles/*.md), or None when the kernel source or its headers changed
+    since then."""
     import glob
-    import hashlib
-    digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    digest = source_digest(source)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             if not line.startswith("traffic-record:"):

@@ -17,11 +17,18 @@ namespace cowa {
 // neighbours in the logical order (which read the same tiles) share an L2.
 constexpr int kXcds = 8;  // XCDs of an MI355X
 
-// chunk = units_per_chunk * per_unit, with units_per_chunk up to max_units
-// while every XCD still gets four chunks or more
+// chunk = k units of per_unit workgroups, 1 <= k <= max_units: at least
+// enough units to fill one XCD's 32 compute units (workgroups of neighbouring
+// units read the same tiles, and only those running together share the L2),
+// and beyond that only as many as leave every XCD 16 chunks or more, so that
+// the heavy-first order evens out across the XCDs.
 inline int32_t xcd_chunk(int64_t per_unit, int64_t units, int64_t max_units) {
-  int64_t k = units / (4 * kXcds);
-  k = k < 1 ? 1 : (k > max_units ? max_units : k);
+  const int64_t fill = (32 + per_unit - 1) / per_unit;
+  const int64_t spread = units / (16 * kXcds);
+  int64_t k = spread < max_units ? spread : max_units;
+  k = k > fill ? k : fill;
+  k = k > max_units ? max_units : k;
+  k = k < 1 ? 1 : k;
   return (int32_t)(per_unit * k);
 }
 // grid size: the logical count padded to whole rounds of kXcds chunks

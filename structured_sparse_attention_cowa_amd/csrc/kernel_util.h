@@ -34,12 +34,15 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 }
 
 // Logical index of workgroup i under the chunked XCD order (see kXcds), or
-// -1 for a padding workgroup past total.
+// -1 for a padding workgroup past total.  Round j deals chunks 8j .. 8j+7 to
+// the XCDs in alternating directions, so with heavy-first work the XCD that
+// takes a round's heaviest chunk takes the next round's lightest.
 __device__ __forceinline__ int xcd_logical(int i, int chunk, int total) {
   const int xcd = i % kXcds;
   const int r = i / kXcds;
   const int j = r / chunk;
-  const int l = (j * kXcds + xcd) * chunk + (r - j * chunk);
+  const int c = (j & 1) ? kXcds - 1 - xcd : xcd;
+  const int l = (j * kXcds + c) * chunk + (r - j * chunk);
   return l < total ? l : -1;
 }
 
