@@ -2,6 +2,8 @@
 // Every check runs on the host before anything is launched.
 #include <math.h>
 
+#include <vector>
+
 #include "cowa_internal.h"
 
 namespace cowa {
@@ -26,10 +28,12 @@ int32_t resolve_n_bands(const cowa_pattern* p) {
 }
 
 // A grid of `total` workgroups in the chunked XCD order (chunks of at most 8
-// units of per_unit workgroups each) is padded to whole rounds of kXcds
-// chunks; the padded count must fit the 31-bit workgroup index.
+// units of per_unit workgroups, or of at most 64 workgroups when chosen by
+// balanced_chunks) is padded to whole rounds of kXcds chunks; the padded count
+// must fit the 31-bit workgroup index.
 bool grid_fits(int64_t total, int64_t per_unit) {
-  return total + (int64_t)kXcds * 8 * per_unit <= 0x7fffffffLL;
+  const int64_t chunk = 8 * per_unit > 64 ? 8 * per_unit : 64;
+  return total + (int64_t)kXcds * chunk <= 0x7fffffffLL;
 }
 
 int32_t resolve_band(const cowa_pattern* p) {
@@ -118,6 +122,101 @@ static cowa_status plan_size_memo(const cowa_pattern* p, int32_t n, int32_t h_kv
   return COWA_OK;
 }
 
+// Chunk sizes of the forward and dQ grids, chosen against the work of each
+// workgroup.  Chunks are dealt to the XCDs in rounds of kXcds, alternating
+// direction (xcd_logical), and the work of a workgroup is the row length of
+// its (KV head, query tile) in the plan plus a fixed cost of a few steps, so
+// the host can total every XCD's work for a candidate chunk size.  Sizes from
+// 32 workgroups (one per compute unit of an XCD: those running together share
+// its L2) to 64 are tried and the one whose busiest XCD carries the least work
+// is kept (the larger on a tie).  0 asks the launcher for its default.
+struct GridChoice {
+  int32_t fwd, dq;
+};
+
+static double busiest_xcd(const std::vector<double>& prefix, int64_t chunk) {
+  const int64_t n = (int64_t)prefix.size() - 1;
+  double x[kXcds] = {};
+  for (int64_t c = 0, a = 0; a < n; ++c, a += chunk) {
+    const int64_t j = c / kXcds, r = c % kXcds;
+    const int64_t xcd = (j & 1) ? kXcds - 1 - r : r;
+    x[xcd] += prefix[a + chunk < n ? a + chunk : n] - prefix[a];
+  }
+  double m = 0;
+  for (double v : x) m = v > m ? v : m;
+  return m;
+}
+
+static int32_t best_chunk(const std::vector<double>& work) {
+  const int64_t n = (int64_t)work.size();
+  if (n < 2 * kXcds * 32) return 0;  // too few workgroups for the search to matter
+  std::vector<double> prefix(n + 1, 0.0);
+  for (int64_t i = 0; i < n; ++i) prefix[i + 1] = prefix[i] + work[i];
+  int32_t best = 0;
+  double best_v = 0;
+  for (int32_t c = 32; c <= 64; ++c) {
+    const double v = busiest_xcd(prefix, c);
+    if (best == 0 || v <= best_v * (1 + 1e-9)) {
+      best = c;
+      best_v = v;
+    }
+  }
+  return best;
+}
+
+static cowa_status balanced_chunks(const cowa_pattern* p, int32_t N, int32_t H_kv_local,
+                                   int32_t B, int32_t H_q, GridChoice* out) {
+  struct Entry {
+    cowa_pattern p;
+    int32_t n, h, b, hq;
+    GridChoice g;
+    bool used;
+  };
+  thread_local Entry memo[8] = {};
+  thread_local int next = 0;
+  for (auto& e : memo) {
+    if (e.used && e.n == N && e.h == H_kv_local && e.b == B && e.hq == H_q &&
+        e.p.n_ctx == p->n_ctx && e.p.sink == p->sink && e.p.window == p->window &&
+        e.p.band == p->band && e.p.h_kv_global == p->h_kv_global &&
+        e.p.kv_head_offset == p->kv_head_offset && e.p.mode == p->mode &&
+        e.p.n_bands == p->n_bands) {
+      *out = e.g;
+      return COWA_OK;
+    }
+  }
+  const int32_t nqt = (N + kFwdBlockM - 1) / kFwdBlockM;
+  std::vector<int32_t> rp((size_t)H_kv_local * nqt + 1);
+  int64_t nnz = 0;
+  cowa_status st = plan_impl(p, N, H_kv_local, kFwdBlockM, kFwdBlockN, rp.data(), nullptr,
+                             nullptr, 0, &nnz);
+  if (st != COWA_OK) return st;
+  const int32_t G = H_q / H_kv_local;
+  const double fixed = 4.0;  // steps' worth of set-up per workgroup
+  auto work_of = [&](int32_t qi, int32_t hq) {
+    const int32_t h = hq / G;
+    return fixed + (rp[(size_t)h * nqt + qi + 1] - rp[(size_t)h * nqt + qi]);
+  };
+  const int64_t total = (int64_t)B * H_q * nqt;
+  std::vector<double> w(total);
+  // forward order: query tiles heavy first, then (sequence, head)
+  for (int64_t i = 0; i < total; ++i) {
+    const int32_t qi = nqt - 1 - (int32_t)(i / ((int64_t)B * H_q));
+    w[i] = work_of(qi, (int32_t)(i % ((int64_t)B * H_q)) % H_q);
+  }
+  GridChoice g;
+  g.fwd = best_chunk(w);
+  // dQ order: sequence, then query tiles heavy first, then head
+  for (int64_t i = 0; i < total; ++i) {
+    const int64_t rem = i % ((int64_t)nqt * H_q);
+    w[i] = work_of(nqt - 1 - (int32_t)(rem / H_q), (int32_t)(rem % H_q));
+  }
+  g.dq = best_chunk(w);
+  memo[next] = Entry{*p, N, H_kv_local, B, H_q, g, true};
+  next = (next + 1) & 7;
+  *out = g;
+  return COWA_OK;
+}
+
 static bool strides_ok(const int64_t* s, int n) {
   for (int i = 0; i < n; ++i)
     if (s[i] < 0) return false;
@@ -180,6 +279,14 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
   fp.n_bands = resolve_n_bands(p);
   fp.cu_seqlens = cu_seqlens;
   fp.total_tokens = total_tokens;
+  // packed sequences: lengths are on the device, so the launcher's default order
+  fp.xcd_chunk = 0;
+  if (!cu_seqlens) {
+    GridChoice gc;
+    st = balanced_chunks(p, N, H_kv_local, B, H_q, &gc);
+    if (st != COWA_OK) return st;
+    fp.xcd_chunk = gc.fwd;
+  }
   fp.scale = softmax_scale;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_fwd(fp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
@@ -571,6 +678,14 @@ static cowa_status bwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr,
   bp.scale_log2 = softmax_scale * 1.4426950408889634f;
   bp.cu_seqlens = cu_seqlens;
   bp.total_tokens = total_tokens;
+  bp.xcd_chunk_q = 0;
+  bp.xcd_chunk_kv = 0;
+  if (!cu_seqlens) {
+    GridChoice gc;
+    st = balanced_chunks(p, N, H_kv_local, B, H_q, &gc);
+    if (st != COWA_OK) return st;
+    bp.xcd_chunk_q = gc.dq;
+  }
   return launch_bwd(bp, d, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
 }
 

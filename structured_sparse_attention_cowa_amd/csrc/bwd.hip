@@ -733,8 +733,9 @@ int launch_bwd_d(const BwdParams& p_in, hipStream_t s) {
   // KV_CHUNK_TILES key tiles with all their (sequence, head) pairs (dK/dV)
   BwdParams p = p_in;
   const int64_t kv_units = p.nkt_kv + (int64_t)p.n_sink_tiles * (p.nch - 1);
-  p.xcd_chunk_q = xcd_chunk(p.Hq, (int64_t)p.B * p.nqt, 8);
-  p.xcd_chunk_kv = xcd_chunk((int64_t)p.B * p.Hkv, kv_units, KV_CHUNK_TILES);
+  if (p.xcd_chunk_q <= 0) p.xcd_chunk_q = xcd_chunk(p.Hq, (int64_t)p.B * p.nqt, 8);
+  if (p.xcd_chunk_kv <= 0)
+    p.xcd_chunk_kv = xcd_chunk((int64_t)p.B * p.Hkv, kv_units, KV_CHUNK_TILES);
   hipLaunchKernelGGL(cowa_bwd_delta_kernel<D>, dim3((unsigned)(p.npad / DELTA_ROWS), p.Hq, p.B),
                      dim3(256), 0, s, p);
   const dim3 gq((unsigned)xcd_grid((int64_t)p.B * p.nqt * p.Hq, p.xcd_chunk_q));

@@ -74,7 +74,7 @@ struct FwdParams {
   // NULL: the batched layout ([B, N, ...] with the b strides).
   const int32_t* cu_seqlens;
   int32_t total_tokens;
-  int32_t xcd_chunk;  // workgroup order: chunks of this many go to one XCD (set by launch_fwd)
+  int32_t xcd_chunk;  // workgroup order: chunks of this many go to one XCD (0: launch_fwd's default)
   float scale;       // softmax scale (natural-log domain)
   float scale_log2;  // scale * log2(e)
 };
@@ -156,7 +156,7 @@ struct BwdParams {
   const int32_t* cu_seqlens;
   int32_t total_tokens;
   int32_t B, N, Hq, Hkv, G, nqt, nkt_kv, nqt_kv, npad;
-  int32_t xcd_chunk_q, xcd_chunk_kv;  // workgroup chunks per XCD (set by launch_bwd)
+  int32_t xcd_chunk_q, xcd_chunk_kv;  // workgroup chunks per XCD (0: launch_bwd's default)
   int32_t n_sink_tiles;  // leading key tiles whose step lists are split (0: none)
   int32_t nch;           // parts per split key tile
   int32_t sink, window, band, kv_head_offset, causal;

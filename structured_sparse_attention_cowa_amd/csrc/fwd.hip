@@ -388,10 +388,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 }  // namespace
 
 int launch_fwd(const FwdParams& p_in, int d, int o_f32, void* stream) {
-  // a chunk is up to 8 query tiles with all their (sequence, head) pairs
+  // default chunk (packed sequences): whole query tiles with all their
+  // (sequence, head) pairs, up to 8 of them
   FwdParams p = p_in;
   const int64_t per_qi = (int64_t)p.B * p.Hq;
-  p.xcd_chunk = xcd_chunk(per_qi, p.nqt, 8);
+  if (p.xcd_chunk <= 0) p.xcd_chunk = xcd_chunk(per_qi, p.nqt, 8);
   const dim3 grid((unsigned)xcd_grid(per_qi * p.nqt, p.xcd_chunk));
   const dim3 block(NTHREADS);
   hipStream_t s = static_cast<hipStream_t>(stream);

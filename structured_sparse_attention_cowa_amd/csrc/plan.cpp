@@ -29,10 +29,11 @@ cowa_status plan_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int3
   const int32_t L = resolve_band(p);
   const int32_t nqt = (n + bm - 1) / bm;
   const int32_t nkt = (n + bn - 1) / bn;
-  const bool write = row_ptr != nullptr;
+  const bool write = row_ptr != nullptr && col != nullptr;  // the whole plan
+  const bool rows_only = row_ptr != nullptr && col == nullptr;  // row_ptr alone
   std::vector<int32_t> touch(nkt + 1), cover(nkt + 1);
   int64_t nnz = 0;
-  if (write) row_ptr[0] = 0;
+  if (write || rows_only) row_ptr[0] = 0;
   for (int32_t h = 0; h < h_kv_local; ++h) {
     const HeadPattern hp = head_pattern(p->sink, p->window, L,
                                         band_slot(p->kv_head_offset + h, resolve_n_bands(p)),
@@ -88,7 +89,7 @@ cowa_status plan_impl(const cowa_pattern* p, int32_t n, int32_t h_kv_local, int3
         touch[kmax + 1] = 0;
         cover[kmax + 1] = 0;
       }
-      if (write) {
+      if (write || rows_only) {
         if (nnz > 0x7fffffff) return COWA_ERR_CAPACITY;
         row_ptr[(int64_t)h * nqt + qi + 1] = (int32_t)nnz;
       }

@@ -59,3 +59,14 @@ def test_xcd_chunk_sizes_of_the_workloads():
     assert xcd_chunk(40, 128, 8) == 40
     # long sequences with few heads get more units per chunk, up to the cap
     assert xcd_chunk(1, 1 << 16, 8) == 8
+
+
+@pytest.mark.parametrize("total", [1, 255, 256, 2560, 5120, 2049, 10007])
+def test_xcd_order_any_chunk_size(total):
+    # the host may pick any chunk from 32 to 64 workgroups (balanced against
+    # the plan's row lengths): the order stays a bijection for every size
+    for chunk in range(32, 65):
+        grid = xcd_grid(total, chunk)
+        i = np.arange(grid)
+        lg = xcd_logical(i, chunk, total)
+        assert np.array_equal(np.sort(lg[lg >= 0]), np.arange(total))
