@@ -48,10 +48,6 @@ constexpr int NTHREADS = 64 * NWAVES;
 // maximum is used for the sum and for the output).
 constexpr float RESCALE_LOG2 = 8.0f;
 
-#ifndef COWA_SCHED
-#define COWA_SCHED 1
-#endif
-
 // LDS swizzles (16-byte chunk index XOR a function of the row), chosen so
 // that the reads below hit distinct banks whether the LDS serves 128 or 256
 // bytes per cycle.  K: 16 consecutive rows read one column chunk.  V: the
@@ -325,7 +321,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
-#if COWA_SCHED
     // interleave: MFMAs of S(e+1) with the softmax VALU of S(e), then the
     // P.V MFMAs with their transposed V reads
 #pragma unroll
@@ -336,16 +331,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
-#if COWA_SCHED == 2
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#endif
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
-#endif
     c_cur = c_n1;
     c_n1 = c_n2;
     __builtin_amdgcn_s_waitcnt(0);
