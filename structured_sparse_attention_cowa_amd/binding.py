@@ -186,7 +186,8 @@ def _stream_ptr(stream):
 
 
 def _strides(t, ndim_keep):
-    assert t.stride(-1) == 1, "last (head-dim) axis must be contiguous"
+    if t.stride(-1) != 1:
+        raise ValueError("the last (head-dim) axis must be contiguous")
     return list(t.stride()[:ndim_keep])
 
 
