@@ -147,9 +147,13 @@ static double busiest_xcd(const std::vector<double>& prefix, int64_t chunk) {
   return m;
 }
 
+// Grids outside [2 * kXcds * 32, kMaxSearched] workgroups keep the default:
+// too few for the search to matter, or so many that it would cost more host
+// time and memory than it could save (and every XCD then gets many chunks).
+constexpr int64_t kMaxSearched = 1 << 20;
+
 static int32_t best_chunk(const std::vector<double>& work) {
   const int64_t n = (int64_t)work.size();
-  if (n < 2 * kXcds * 32) return 0;  // too few workgroups for the search to matter
   std::vector<double> prefix(n + 1, 0.0);
   for (int64_t i = 0; i < n; ++i) prefix[i + 1] = prefix[i] + work[i];
   int32_t best = 0;
@@ -185,6 +189,11 @@ static cowa_status balanced_chunks(const cowa_pattern* p, int32_t N, int32_t H_k
     }
   }
   const int32_t nqt = (N + kFwdBlockM - 1) / kFwdBlockM;
+  const int64_t total = (int64_t)B * H_q * nqt;
+  if (total < 2 * kXcds * 32 || total > kMaxSearched) {
+    *out = GridChoice{0, 0};
+    return COWA_OK;
+  }
   std::vector<int32_t> rp((size_t)H_kv_local * nqt + 1);
   int64_t nnz = 0;
   cowa_status st = plan_impl(p, N, H_kv_local, kFwdBlockM, kFwdBlockN, rp.data(), nullptr,
@@ -196,7 +205,6 @@ static cowa_status balanced_chunks(const cowa_pattern* p, int32_t N, int32_t H_k
     const int32_t h = hq / G;
     return fixed + (rp[(size_t)h * nqt + qi + 1] - rp[(size_t)h * nqt + qi]);
   };
-  const int64_t total = (int64_t)B * H_q * nqt;
   std::vector<double> w(total);
   // forward order: query tiles heavy first, then (sequence, head)
   for (int64_t i = 0; i < total; ++i) {
