@@ -1,6 +1,6 @@
 /*
  * cowa.h - C ABI of libcowa, a gfx950 (MI355X) implementation of CoWindow
- * Attention (CoWA) prefill and decode.
+ * Attention (CoWA): prefill, decode and the prefill's backward.
  *
  * The method.  "CoWindow Attention: Full Causal Coverage Is a Collective
  * Property" (Abstract) and "Splitting long-range windows across KV heads
@@ -44,7 +44,8 @@
  *    empty (cu_seqlens[b+1] == cu_seqlens[b]); it produces no rows.
  *  - bf16 means IEEE bfloat16 stored as 2 bytes.  Strides are in elements;
  *    the last (head-dim) axis is always contiguous.
- *  - The library is stateless and thread-safe.
+ *  - The library is thread-safe.  Its only state is per-thread caches of
+ *    plan sizes and launch-order choices per shape, which change no result.
  */
 #ifndef COWA_H
 #define COWA_H
@@ -60,7 +61,7 @@ typedef enum {
   COWA_OK = 0,
   COWA_ERR_INVALID_ARG = 1,   /* a size, pointer or pattern field is invalid */
   COWA_ERR_UNSUPPORTED = 2,   /* valid but not compiled (head dim, tile shape, group size) */
-  COWA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small */
+  COWA_ERR_WORKSPACE = 3,     /* decode or backward workspace missing, misaligned or too small */
   COWA_ERR_PLAN_MISMATCH = 4, /* plan size does not match pattern/shape/tile */
   COWA_ERR_HIP = 5,           /* a HIP launch failed */
   COWA_ERR_CAPACITY = 6       /* caller's plan buffers are too small */
