@@ -60,3 +60,60 @@ def test_graph_replays_match_eager(lib):
         for name, a, b in zip(("o", "lse", "dq", "dk", "dv", "decode o", "decode lse"), ref,
                               outs()):
             assert torch.equal(a, b), f"replay {rep}: {name}"
+
+
+def test_graph_replays_match_eager_varlen(lib):
+    """The packed forward and backward captured together (a training step on
+    a packed batch), replayed against their eager results."""
+    import torch
+    lens = np.array([700, 0, 33, 1500, 256], np.int64)
+    T, max_len = int(lens.sum()), int(lens.max())
+    Hq, Hkv, d = 8, 2, 64
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    x = W.random_prefill(504, 1, T, Hq, Hkv, d)
+    q, k, v = bits_to_dev(x.q_bits[0]), bits_to_dev(x.k_bits[0]), bits_to_dev(x.v_bits[0])
+    do = bits_to_dev(W.grad_output(505, 1, T, Hq, d)[0])
+    p = C.make_pattern(max_len, 16, 128, 0, 4, 2)
+    bm, bn = C.cowa_fwd_block_sizes(d)
+    bmk, bnk = C.cowa_bwd_block_sizes(d)
+    rp, col, fl = [torch.from_numpy(a).cuda() for a in C.cowa_plan(p, max_len, Hkv, bm, bn)]
+    rpk, colk, flk = [torch.from_numpy(a).cuda()
+                      for a in C.cowa_plan_kv(p, max_len, Hkv, bmk, bnk)]
+    ws = torch.empty(C.cowa_bwd_workspace_size(p, len(lens), Hq, Hkv, max_len),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+
+    def work():
+        C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse, cu, max_len,
+                          scale)
+        C.cowa_bwd_varlen(p, rp, col, fl, col.numel(), bm, bn, rpk, colk, flk, colk.numel(),
+                          bmk, bnk, q, k, v, o, do, lse, dq, dk, dv, cu, max_len, scale, ws)
+
+    tensors = (o, lse, dq, dk, dv)
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in tensors]
+    assert all(torch.isfinite(t.float()).all() for t in ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in tensors:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), ref, tensors):
+            assert torch.equal(a, b), f"replay {rep}: {name}"
