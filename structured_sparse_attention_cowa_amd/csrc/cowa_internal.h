@@ -42,7 +42,7 @@ constexpr int kFwdBlockN = 64;
 
 // Decode: largest visible-key chunk one workgroup handles, and the largest
 // GQA group size compiled.
-constexpr int kDecodeChunkMax = 512;
+constexpr int kDecodeChunkMax = 768;
 constexpr int kDecodeMaxGroup = 8;
 
 cowa_status validate_pattern(const cowa_pattern* p, int32_t h_kv_local);
