@@ -353,10 +353,11 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   if (tid < G) p.lsepart[pidx + tid] = (stat_m[tid] + __log2f(stat_l[tid])) * LN2;
 }
 
-// Merge of the chunks of one (sequence, query head) by log-sum-exp.  The
-// chunk log-sum-exps are loaded one per thread, their weights kept in LDS;
-// four groups of 64 threads each sum a quarter of the chunks (all loads in
-// flight at once) and are added in LDS.
+// Merge of the chunks of one (sequence, query head) by log-sum-exp.  Four
+// groups of 64 threads each sum a quarter of the chunks and are added in LDS.
+// Up to 32 chunks, each group requests its chunks' outputs and log-sum-exps
+// together and weights them once the maximum is known; beyond that the
+// log-sum-exps are loaded one per thread first and the weights kept in LDS.
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void cowa_decode_combine(DecodeParams p) {
   constexpr int MAXW = 1024;       // chunk weights held in LDS per pass
@@ -376,47 +377,83 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_combine(DecodeParams p) 
   const int64_t stride_s = (int64_t)p.B * p.Hq;
   const int64_t base = (int64_t)b * p.Hq + hq;
 
-  // maximum chunk log-sum-exp
-  float m = NEG_INF;
-  for (int s2 = tid; s2 < ns; s2 += NTHREADS) m = fmaxf(m, p.lsepart[s2 * stride_s + base]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-
+  const float* op = p.opart + base * D + lane * DPT;
+  float M;
   float o[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) o[i] = 0.f;
-  float wsum = 0.f;
-  const float* op = p.opart + base * D + lane * DPT;
-  for (int s0 = 0; s0 < ns; s0 += MAXW) {
-    const int nb = ns - s0 < MAXW ? ns - s0 : MAXW;
-    for (int i = tid; i < nb; i += NTHREADS) {
-      const float w = __expf(p.lsepart[(s0 + i) * stride_s + base] - M);
-      wts[i] = w;
-      wsum += w;
+  float wsum = 0.f;   // summed over the wavefront below
+  if (ns <= 4 * 8) {
+    // At most eight chunks per group: the partial outputs and their
+    // log-sum-exps are all requested before the maximum is known (one memory
+    // round trip); every lane of a group holds the same eight weights.
+    float v[8][DPT];
+    float lw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = wave + 4 * u;
+      lw[u] = NEG_INF;
+      if (k < ns) {
+        lw[u] = p.lsepart[k * stride_s + base];
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) v[u][i] = op[(int64_t)k * stride_s * D + i];
+      }
     }
+    float m = NEG_INF;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, lw[u]);
+    if (lane == 0) red[wave] = m;
     __syncthreads();
-    // group `wave` takes chunks wave, wave + 4, ...
-    int k = wave;
-    for (; k + 4 * 7 < nb; k += 4 * 8) {
-      float v[8][DPT];
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float ws = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u)
+      if (wave + 4 * u < ns) {
+        const float w = __expf(lw[u] - M);
+        ws += w;
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) v[u][i] = op[(int64_t)(s0 + k + 4 * u) * stride_s * D + i];
+        for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(w, v[u][i], o[i]);
+      }
+    if (lane == 0) wsum = ws;
+  } else {
+    // maximum chunk log-sum-exp
+    float m = NEG_INF;
+    for (int s2 = tid; s2 < ns; s2 += NTHREADS) m = fmaxf(m, p.lsepart[s2 * stride_s + base]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+
+    for (int s0 = 0; s0 < ns; s0 += MAXW) {
+      const int nb = ns - s0 < MAXW ? ns - s0 : MAXW;
+      for (int i = tid; i < nb; i += NTHREADS) {
+        const float w = __expf(p.lsepart[(s0 + i) * stride_s + base] - M);
+        wts[i] = w;
+        wsum += w;
+      }
+      __syncthreads();
+      // group `wave` takes chunks wave, wave + 4, ...
+      int k = wave;
+      for (; k + 4 * 7 < nb; k += 4 * 8) {
+        float v[8][DPT];
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wts[k + 4 * u], v[u][i], o[i]);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) v[u][i] = op[(int64_t)(s0 + k + 4 * u) * stride_s * D + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) o[i] = __builtin_fmaf(wts[k + 4 * u], v[u][i], o[i]);
+      }
+      for (; k < nb; k += 4)
+#pragma unroll
+        for (int i = 0; i < DPT; ++i)
+          o[i] = __builtin_fmaf(wts[k], op[(int64_t)(s0 + k) * stride_s * D + i], o[i]);
+      __syncthreads();
     }
-    for (; k < nb; k += 4)
-#pragma unroll
-      for (int i = 0; i < DPT; ++i)
-        o[i] = __builtin_fmaf(wts[k], op[(int64_t)(s0 + k) * stride_s * D + i], o[i]);
-    __syncthreads();
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
