@@ -68,6 +68,16 @@ def test_decode_edge_lengths(lib):
                 lens=[1, 2048, 8, 9, 64, 65], n_ctx=2048)
 
 
+@pytest.mark.parametrize("n_max", [2048, 2112])
+def test_decode_combine_chunk_count_boundary(lib, n_max):
+    """Full-causal mode with one KV head: 64-key chunks, so the longest
+    sequence has exactly 32 chunks at n_max = 2048 (the combine's path that
+    loads every chunk at once, all four groups full) and 33 at n_max = 2112
+    (the general path); shorter sequences in the batch have fewer."""
+    _small_case(60, 4, n_max, 5, 1, 128, 8, 64, 1, mode=1,
+                lens=[n_max, n_max - 63, 1985, 70], n_ctx=n_max)
+
+
 def test_decode_group_sizes(lib):
     for G in (1, 2, 3, 6, 7, 8):
         _small_case(10 + G, 2, 1500, G * 2, 2, 128, 4, 100, 4, off=2)
