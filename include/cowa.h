@@ -104,6 +104,23 @@ int32_t cowa_band_length(const cowa_pattern* p);
  * head dim d; COWA_ERR_UNSUPPORTED if d is not compiled (64 and 128 are). */
 cowa_status cowa_fwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n);
 
+/* ---- cowa_visible_ranges: the keys one query row sees (host only) -------
+ * The visible keys of query position t for local KV head h (global index
+ * g = kv_head_offset + h), as three disjoint half-open key ranges in
+ * ascending order: [lo[0], hi[0]) the sink, [lo[1], hi[1]) the long-range
+ * window (the keys of the head's band that the sink and the local window do
+ * not already hold) and [lo[2], hi[2]) the local window; an empty range has
+ * lo == hi.  In COWA_MODE_CAUSAL range 2 is [0, t+1) and the others are
+ * empty.  The pattern is position arithmetic only (news page, mechanism
+ * paragraph; Abstract: shared windows plus one band per KV head).  The decode
+ * kernels evaluate the same function on the device for t = len - 1, so a
+ * caller can see exactly which cache rows a decode step reads (and which it
+ * will never read again).
+ * COWA_ERR_INVALID_ARG for an invalid pattern, h outside
+ * [0, h_kv_global - kv_head_offset), t < 0 or a null lo / hi. */
+cowa_status cowa_visible_ranges(const cowa_pattern* p, int32_t h, int32_t t, int32_t lo[3],
+                                int32_t hi[3]);
+
 /* ---- cowa_plan: visible-tile lists (host only, no device work) ----------
  * For local KV heads h = 0..h_kv_local-1 (global g = kv_head_offset + h) and
  * query tiles qi = 0..ceil(n/block_m)-1, lists the key tiles kj whose block

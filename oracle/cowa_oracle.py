@@ -46,8 +46,13 @@ textbook dense causal softmax, closed-form band-only case, softmax identities
 checked against scipy).  The backward (attention_backward and its row- and
 key-sampled forms) is pinned by float64 autograd where CoWA reduces to dense
 causal attention, central finite differences of the forward, GQA sums of
-single-head problems and invariance to a common shift of the value rows; the
-KV retention mask by brute force over all later queries.  Numeric O/LSE
+single-head problems and invariance to a common shift of the value rows.
+The error-bound helpers: the D-sensitivity (_d_sensitivity, eq, ek) by its
+closed form when every row's softmax is uniform and by shifting D in the
+backward (the bound holds, and is attained when q, k have one sign); the KV
+retention mask (brute force over all later queries) by its closed form.
+visible_code_sums (zero-query attention as integer sums) by the dense
+predicate and the merged interval form.  Numeric O/LSE
 values for the benchmark workloads are not printed by the pages; for those
 the definition below plus the reductions above are the pins.
 """
@@ -242,31 +247,39 @@ def tile_counts_intervals(n: int, g: int, p: Pattern, bm: int, bn: int) -> np.nd
     return counts
 
 
+def row_windows(t, g: int, p: Pattern):
+    """Visible keys of query positions t (int array) as disjoint [a, b) key
+    intervals, one array pair per window: sink, then band minus sink, then
+    local window minus the other two (a >= b: empty).  The same windows as
+    visible_intervals, written per window instead of merged, so that plain
+    interval sums count each key once.  Causal mode: one interval [0, t+1)."""
+    t = np.asarray(t, dtype=np.int64)
+    if p.mode == MODE_CAUSAL:
+        return [(np.zeros_like(t), t + 1)]
+    L = resolved_band(p)
+    sink_b = np.minimum(p.sink, t + 1)
+    sink = (np.zeros_like(t), sink_b)
+    loc_a = np.maximum(np.maximum(0, t - p.window + 1), sink_b)
+    loc = (loc_a, np.maximum(t + 1, loc_a))
+    ivs = [sink, loc]
+    if L > 0:
+        bi = band_index(g, p)
+        ba = np.maximum(t - (p.window + (bi + 1) * L) + 1, sink_b)
+        bb = np.minimum(t - (p.window + bi * L) + 1, loc_a)
+        bb = np.maximum(bb, ba)
+        ivs.append((ba, bb))
+    return ivs
+
+
 def tile_counts_intervals_fast(n: int, g: int, p: Pattern, bm: int, bn: int) -> np.ndarray:
     """Same as tile_counts_intervals, vectorised over rows (for 32K-128K).
 
-    Each window of row t is an interval [a_t, b_t); the per-window intervals
-    are made disjoint first (sink, then band minus sink, then local minus the
-    other two) so that plain +1/-1 difference marks count each key once.
+    Each window of row t is an interval [a_t, b_t) (row_windows, made
+    disjoint) so that plain +1/-1 difference marks count each key once.
     """
     nqt = -(-n // bm)
     nkt = -(-n // bn)
-    t = np.arange(n, dtype=np.int64)
-    if p.mode == MODE_CAUSAL:
-        ivs = [(np.zeros_like(t), t + 1)]
-    else:
-        L = resolved_band(p)
-        sink_b = np.minimum(p.sink, t + 1)
-        sink = (np.zeros_like(t), sink_b)
-        loc_a = np.maximum(np.maximum(0, t - p.window + 1), sink_b)
-        loc = (loc_a, np.maximum(t + 1, loc_a))
-        ivs = [sink, loc]
-        if L > 0:
-            bi = band_index(g, p)
-            ba = np.maximum(t - (p.window + (bi + 1) * L) + 1, sink_b)
-            bb = np.minimum(t - (p.window + bi * L) + 1, loc_a)
-            bb = np.maximum(bb, ba)
-            ivs.append((ba, bb))
+    ivs = row_windows(np.arange(n, dtype=np.int64), g, p)
     counts = np.zeros((nqt, nkt), dtype=np.int64)
     for qi in range(nqt):
         r0, r1 = qi * bm, min((qi + 1) * bm, n)
@@ -279,6 +292,30 @@ def tile_counts_intervals_fast(n: int, g: int, p: Pattern, bm: int, bn: int) -> 
         per_key = np.cumsum(diff[:-1])
         counts[qi] = per_key.reshape(nkt, bn).sum(axis=1)
     return counts
+
+
+def visible_code_sums(rows, g: int, p: Pattern, codes: np.ndarray):
+    """Per query position t in rows: the number of keys head g sees and the
+    sum of codes[j] over those keys (codes: integer array [n_keys, c], keys
+    0..n_keys-1, n_keys > max(rows)).
+
+    This is the exact outcome of attention with a zero query: every visible
+    score is 0, so the softmax is uniform over the visible set ([SF] paragraph
+    on what CoWA does not claim: each head's softmax runs over its own visible
+    set), LSE = ln(count) and O * count = sum of the visible value rows.
+    Computed from row_windows with prefix sums over keys.
+    Returns counts int64 [R] and sums int64 [R, c]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    codes = np.asarray(codes)
+    prefix = np.zeros((codes.shape[0] + 1, codes.shape[1]), dtype=np.int64)
+    np.cumsum(codes, axis=0, out=prefix[1:])
+    counts = np.zeros(len(rows), dtype=np.int64)
+    sums = np.zeros((len(rows), codes.shape[1]), dtype=np.int64)
+    for a, b in row_windows(rows, g, p):
+        b = np.maximum(a, b)
+        counts += b - a
+        sums += prefix[b] - prefix[a]
+    return counts, sums
 
 
 def tile_lists(n: int, h_kv_local: int, p: Pattern, bm: int, bn: int, method: str = "auto"):
@@ -427,8 +464,12 @@ def default_scale(d: int) -> float:
 # --------------------------------------------------------------------------
 
 
-def attention_backward(q, k, v, do, p: Pattern, scale: float, magnitudes: bool = False):
+def attention_backward(q, k, v, do, p: Pattern, scale: float, magnitudes: bool = False,
+                       d_shift=None):
     """Full backward in float64 for moderate sizes (dense per head).
+
+    d_shift: optional [B, N, H_q] array added to D_t before dS is formed (an
+    error in D, to measure how the gradients respond to one; None: exact).
 
     With magnitudes=True it also returns, for each gradient, the sum of the
     absolute values of the terms it is the sum of (scale sum_j |dS_tj| |k_j|,
@@ -465,6 +506,8 @@ def attention_backward(q, k, v, do, p: Pattern, scale: float, magnitudes: bool =
             o = P @ v[b, :, h]
             dP = do[b, :, hq] @ v[b, :, h].T
             D = (do[b, :, hq] * o).sum(axis=1, keepdims=True)
+            if d_shift is not None:
+                D = D + np.asarray(d_shift, np.float64)[b, :, hq][:, None]
             dS = P * (dP - D)
             dq[b, :, hq] = scale * dS @ k[b, :, h]
             dk[b, :, h] += scale * dS.T @ q[b, :, hq]

@@ -34,7 +34,7 @@ EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
             "cowa_bwd_workspace_size", "cowa_bwd", "cowa_bwd_varlen", "cowa_kv_window_rows",
             "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window",
-            "cowa_fwd_varlen")
+            "cowa_fwd_varlen", "cowa_visible_ranges")
 
 
 class CowaError(RuntimeError):
@@ -120,6 +120,8 @@ def load():
     lib.cowa_decode_window.restype = ctypes.c_int
     lib.cowa_decode_window.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                        P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_visible_ranges.restype = ctypes.c_int
+    lib.cowa_visible_ranges.argtypes = [pat, i32, i32, P(i32), P(i32)]
     lib.cowa_fwd_varlen.restype = ctypes.c_int
     lib.cowa_fwd_varlen.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                     i32, i32, i32, i32, i32, i32, P(i64), f32, vp]
@@ -156,6 +158,13 @@ def cowa_fwd_block_sizes(d: int):
     _check(load().cowa_fwd_block_sizes(d, ctypes.byref(bm), ctypes.byref(bn)),
            "cowa_fwd_block_sizes")
     return bm.value, bn.value
+
+
+def cowa_visible_ranges(p: cowa_pattern, h: int, t: int):
+    """[(lo, hi)] * 3: sink, long-range window and local window of row t."""
+    lo, hi = (ctypes.c_int32 * 3)(), (ctypes.c_int32 * 3)()
+    _check(load().cowa_visible_ranges(ctypes.byref(p), h, t, lo, hi), "cowa_visible_ranges")
+    return [(lo[i], hi[i]) for i in range(3)]
 
 
 def cowa_plan_size(p: cowa_pattern, n: int, h_kv_local: int, block_m: int, block_n: int) -> int:

@@ -93,6 +93,22 @@ extern "C" cowa_status cowa_fwd_block_sizes(int32_t d, int32_t* block_m, int32_t
   return COWA_OK;
 }
 
+extern "C" cowa_status cowa_visible_ranges(const cowa_pattern* p, int32_t h, int32_t t,
+                                           int32_t lo[3], int32_t hi[3]) {
+  if (!p || !lo || !hi || t < 0 || h < 0) return COWA_ERR_INVALID_ARG;
+  cowa_status st = validate_pattern(p, h + 1);
+  if (st != COWA_OK) return st;
+  const HeadPattern hp = head_pattern(p->sink, p->window, resolve_band(p),
+                                      band_slot(p->kv_head_offset + h, resolve_n_bands(p)),
+                                      p->mode == COWA_MODE_CAUSAL);
+  const RowRanges r = row_ranges(hp, t);
+  for (int i = 0; i < 3; ++i) {
+    lo[i] = r.lo[i];
+    hi[i] = r.hi[i];
+  }
+  return COWA_OK;
+}
+
 // Plan sizes of recently seen shapes, per thread, so that checking a plan
 // against its pattern does not rebuild it on every call.
 static cowa_status plan_size_memo(const cowa_pattern* p, int32_t n, int32_t h_kv_local,

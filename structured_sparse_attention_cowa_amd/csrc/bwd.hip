@@ -114,39 +114,6 @@ __global__ __launch_bounds__(256) void cowa_bwd_delta_kernel(BwdParams p) {
   }
 }
 
-// Offsets of the plain 16-byte reads of a swizzled [rows x D] tile feeding
-// an A operand: row 32 blk + (lane % 32), chunk 2 ks + lane / 32.
-template <int D>
-__device__ __forceinline__ void plain_offsets(int l32, int hl, int (&off)[2][D / 16]) {
-  constexpr int NK = D / 16;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      // rows l32 and 32 + l32 share the swizzle: the two blocks differ by a
-      // constant, which the compiler folds into the read's offset field
-      off[blk][ks] = 32 * blk * D + l32 * D + (((2 * ks + hl) ^ swz_both<D>(l32)) * 8);
-    }
-}
-
-// Offsets of the transposing reads feeding an A operand whose k index runs
-// over 16 tile rows (add 16 D per step): half ri, head-dim block db; lane
-// addresses row 8 ri + 4 (lane / 32) + (lane % 16) / 4 at dims
-// 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3.
-template <int D>
-__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2][D / 32]) {
-  constexpr int ND = D / 32;
-  const int hl = lane >> 5, r16 = lane & 15, gi = (lane >> 4) & 1;
-#pragma unroll
-  for (int ri = 0; ri < 2; ++ri)
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int row = 8 * ri + 4 * hl + (r16 >> 2);
-      const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
-      off[ri][db] = row * D + (((d >> 3) ^ swz_both<D>(row)) * 8) + (d & 7);
-    }
-}
-
 // An empty use of loaded registers: the loads must have completed here, so
 // the tile loops that follow start with no register load in flight.
 template <int N>

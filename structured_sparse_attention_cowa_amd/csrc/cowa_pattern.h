@@ -107,6 +107,40 @@ COWA_HD int32_t row_count(const RowRanges& r) {
   return (r.hi[0] - r.lo[0]) + (r.hi[1] - r.lo[1]) + (r.hi[2] - r.lo[2]);
 }
 
+// Masks of partial tiles.  Within a tile, the keys (or queries) one lane
+// handles fall into at most three intervals of the element offset o in
+// [0, 64): the sink, the local window and the band of vis_g(t, j).  The
+// kernels fold them into one 64-bit mask (bit o set: visible).  Host and
+// device compile the same functions.
+
+// Bits [lo, hi) of a 64-bit mask, with lo and hi clamped to [0, 64].
+COWA_HD uint64_t bit_range(int32_t lo, int32_t hi) {
+  lo = imin(imax(lo, 0), 64);
+  hi = imin(imax(hi, lo), 64);
+  const int32_t w = hi - lo;  // lo <= 63 whenever w > 0
+  return w == 0 ? 0ull : (((2ull << (w - 1)) - 1ull) << lo);
+}
+
+// Row form: query t, element o is key j = base + o.
+COWA_HD uint64_t row_visible_bits(const HeadPattern& hp, int32_t t, int32_t base) {
+  const int32_t d0 = t - base;  // o <= d0 is j <= t
+  if (hp.causal) return bit_range(0, d0 + 1);
+  // a window longer than d0 + 65 covers the same offsets (and keeps d0 - w in
+  // range); the band lies at distances >= W >= 1, so it is causal by itself
+  const int32_t w = imin(hp.window, imax(d0, 0) + 65);
+  return bit_range(0, imin(hp.sink - base, d0 + 1)) | bit_range(d0 - w + 1, d0 + 1) |
+         bit_range(d0 - hp.band_hi + 1, d0 - hp.band_lo + 1);
+}
+
+// Column form: key j, element o is query t = base + o.
+COWA_HD uint64_t col_visible_bits(const HeadPattern& hp, int32_t base, int32_t j) {
+  const int32_t c0 = j - base;  // o >= c0 is t >= j
+  if (hp.causal || j < hp.sink) return bit_range(c0, 64);
+  // offsets past 63 do not matter: the window is cut to 64 - c0 (no overflow)
+  const int32_t w = imin(hp.window, 64 - c0);
+  return bit_range(c0, c0 + w) | bit_range(c0 + hp.band_lo, c0 + hp.band_hi);
+}
+
 // Windowed KV cache for decode ("CoWindow Attention: Full Causal Coverage Is
 // a Collective Property", Abstract: lower per-rank decode memory).  For query
 // t, head g with long-range window b sees non-sink keys only at distances

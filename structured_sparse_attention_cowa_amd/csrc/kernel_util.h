@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "cowa_internal.h"
+#include "cowa_layout.h"
 
 namespace cowa {
 namespace kern {
@@ -31,53 +32,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Logical index of workgroup i under the chunked XCD order (see kXcds), or
-// -1 for a padding workgroup past total.  Round j deals chunks 8j .. 8j+7 to
-// the XCDs in alternating directions, so with heavy-first work the XCD that
-// takes a round's heaviest chunk takes the next round's lightest.
-__device__ __forceinline__ int xcd_logical(int i, int chunk, int total) {
-  const int xcd = i % kXcds;
-  const int r = i / kXcds;
-  const int j = r / chunk;
-  const int c = (j & 1) ? kXcds - 1 - xcd : xcd;
-  const int l = (j * kXcds + c) * chunk + (r - j * chunk);
-  return l < total ? l : -1;
-}
-
-// Masking of partial tiles.  Within a tile, the keys (or queries) a lane
-// sees form at most three intervals of the element offset o in [0, 64): the
-// sink, the local window and the band of vis_g(t, j) (cowa_pattern.h).  Each
-// lane folds them into one 64-bit mask; an element is then kept or set to
-// -inf with a sign-extended bit extract and a bitfield insert.
-
-// Bits [lo, hi) of a 64-bit mask, with lo and hi clamped to [0, 64].
-__device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
-  lo = min(max(lo, 0), 64);
-  hi = min(max(hi, lo), 64);
-  const int w = hi - lo;  // lo <= 63 whenever w > 0
-  return w == 0 ? 0ull : (((2ull << (w - 1)) - 1ull) << lo);
-}
-
-// Row form: the lane is query t, element o is key j = base + o.
-__device__ __forceinline__ uint64_t row_visible_bits(const HeadPattern& hp, int t, int base) {
-  const int d0 = t - base;  // o <= d0 is j <= t
-  if (hp.causal) return bit_range(0, d0 + 1);
-  // a window longer than d0 + 65 covers the same offsets (and keeps d0 - w in
-  // range); the band lies at distances >= W >= 1, so it is causal by itself
-  const int w = min(hp.window, max(d0, 0) + 65);
-  return bit_range(0, min(hp.sink - base, d0 + 1)) | bit_range(d0 - w + 1, d0 + 1) |
-         bit_range(d0 - hp.band_hi + 1, d0 - hp.band_lo + 1);
-}
-
-// Column form: the lane is key j, element o is query t = base + o.
-__device__ __forceinline__ uint64_t col_visible_bits(const HeadPattern& hp, int base, int j) {
-  const int c0 = j - base;  // o >= c0 is t >= j
-  if (hp.causal || j < hp.sink) return bit_range(c0, 64);
-  // offsets past 63 do not matter: the window is cut to 64 - c0 (no overflow)
-  const int w = min(hp.window, 64 - c0);
-  return bit_range(c0, c0 + w) | bit_range(c0 + hp.band_lo, c0 + hp.band_hi);
 }
 
 // s if bit o of m is set, else -inf (o is a compile-time constant).
@@ -136,26 +90,6 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint16_t* lo, const uint16_t* hi) {
   const i16x4 a8[2] = {lds_read_tr(lo), lds_read_tr(hi)};
   return __builtin_bit_cast(bf16x8, a8);
-}
-
-// Row-major [rows x 128] bf16 LDS tiles whose 16-byte chunks are XOR-swizzled
-// by this function of the row are free of bank conflicts both for 16-byte
-// reads of one chunk column by 16 consecutive rows and for transposing reads
-// of 4 consecutive rows x 2-4 adjacent chunks.
-// The value is [0, 6, 12, 10][row % 4] ^ ((row / 4) % 4), written with bit
-// operations so that the compiler can bound it (and the offsets built from it).
-__device__ __forceinline__ int swz_both_d128(int row) {
-  const int a = row & 3;
-  return (((a << 2) ^ (a << 1)) & 14) ^ ((row >> 2) & 3);
-}
-
-// The same swizzle for [rows x D] tiles: for D = 64 (8 chunks per row) its low
-// three bits keep both read patterns free of bank conflicts (checked on the
-// host against a model of 128- and 256-byte LDS cycles).
-template <int D>
-__device__ __forceinline__ int swz_both(int row) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  return swz_both_d128(row) & (D / 8 - 1);
 }
 
 }  // namespace kern

@@ -169,6 +169,55 @@ def random_prefill(seed, B, N, H_q, H_kv, d, scale_q=1.0):
     return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
 
 
+# Position codes: value rows that identify their key position.  With a zero
+# query every visible score is equal, so an output row is the mean of the
+# value rows of exactly the visible keys; with 0/1 codes (exact in bf16) the
+# product of that mean and the visible count is an integer the fp32 sums
+# reproduce exactly, which makes the visible set checkable key by key.
+POSITION_CODE_BITS = 18      # positions below 2^18
+N_POSITION_CODES = 2 * POSITION_CODE_BITS + 1
+BF16_ONE_BITS = 0x3F80
+
+
+def position_codes(j, salt: int = 0) -> np.ndarray:
+    """0/1 codes of key positions j: uint8 [len(j), N_POSITION_CODES].
+
+    Columns 0..17: the bits of j.  Columns 18..35: the bits of a
+    multiplicative hash of (j, salt) (a different code per head or sequence
+    when salt differs).  Column 36: the constant 1."""
+    j = np.asarray(j, dtype=np.uint64)
+    nb = POSITION_CODE_BITS
+    h = ((j + np.uint64(salt) * np.uint64(1 << nb)) * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)
+    h = h >> np.uint64(32 - nb)
+    out = np.zeros((len(j), N_POSITION_CODES), dtype=np.uint8)
+    for c in range(nb):
+        out[:, c] = (j >> np.uint64(c)) & np.uint64(1)
+        out[:, nb + c] = (h >> np.uint64(c)) & np.uint64(1)
+    out[:, 2 * nb] = 1
+    return out
+
+
+def position_code_rows(n: int, d: int, salt: int = 0) -> np.ndarray:
+    """Value rows [n, d] as bf16 bits: the position codes of keys 0..n-1 in the
+    first N_POSITION_CODES dimensions, zero in the rest."""
+    assert d >= N_POSITION_CODES and n <= (1 << POSITION_CODE_BITS)
+    out = np.zeros((n, d), dtype=np.uint16)
+    out[:, :N_POSITION_CODES] = position_codes(np.arange(n), salt) * np.uint16(BF16_ONE_BITS)
+    return out
+
+
+def zero_query_inputs(seed, B, N, H_q, H_kv, d) -> PrefillInputs:
+    """Q = 0, K ~ N(0,1) (seeded), V = position codes, salt b * H_kv + h for
+    sequence b and local KV head h."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = to_bf16_bits(rng.standard_normal((B, N, H_kv, d), dtype=np.float32))
+    v = np.zeros((B, N, H_kv, d), dtype=np.uint16)
+    for b in range(B):
+        for h in range(H_kv):
+            v[b, :, h] = position_code_rows(N, d, b * H_kv + h)
+    return PrefillInputs(np.zeros((B, N, H_q, d), dtype=np.uint16), k, v)
+
+
 def grad_output(seed, B, N, H_q, d) -> np.ndarray:
     """Upstream gradient dO for the backward: N(0,1), bf16 bits [B, N, H_q, d]."""
     rng = np.random.Generator(np.random.PCG64(seed))

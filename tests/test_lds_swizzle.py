@@ -1,26 +1,18 @@
-"""Bank-conflict model of the backward kernels' LDS tiles (host only).
+"""Bank-conflict model of the kernels' LDS tiles, on the compiled layout
+functions (csrc/cowa_layout.h built for the host by tests/host_shim.cpp).
 
-The dQ and dK/dV kernels keep row-major [rows x d] bf16 tiles in LDS with the
-16-byte chunks of each row XOR-swizzled by swz(row), and read them two ways:
-16-byte reads of one chunk column by 32 consecutive rows (the plain A operand)
-and 8-byte transposing reads of 4 consecutive rows x 2 adjacent chunks (the
-transposed A operand).  The swizzles below mirror swz_both_d128 and
-swz_both<64> of csrc/kernel_util.h, and the lane patterns mirror plain_offsets
-and tr_offsets of csrc/bwd.hip.  A read instruction is modelled as served in
-groups of consecutive lanes moving B bytes per cycle (B = 128 or 256); a
-conflict is two lanes of one group touching the same 4-byte bank slot at
-different addresses."""
+Tiles are row-major [rows x d] bf16 with the 16-byte chunks of each row
+XOR-swizzled by swz_both(row).  They are read two ways: 16-byte reads of one
+chunk column by 32 consecutive rows (plain_offsets, the plain A operand) and
+8-byte transposing reads of 4 consecutive rows x 2 adjacent chunks
+(tr_offsets, the transposed A operand).  A read instruction is modelled as
+served in groups of consecutive lanes moving B bytes per cycle (B = 128 or
+256); a conflict is two lanes of one group touching the same 4-byte bank slot
+at different addresses."""
 
 import pytest
 
-
-def swz128(row):
-    a = row & 3
-    return (((a << 2) ^ (a << 1)) & 14) ^ ((row >> 2) & 3)
-
-
-def swz(d):
-    return swz128 if d == 128 else (lambda row: swz128(row) & 7)
+from tests import host_shim
 
 
 def conflicts(addrs, width, B):
@@ -38,36 +30,60 @@ def conflicts(addrs, width, B):
     return n
 
 
-def read_patterns(d, sw):
+def lane_offsets(fn, d, n):
+    lib = host_shim.load()
+    out = []
+    for lane in range(64):
+        a = host_shim.int_array(n)
+        getattr(lib, fn)(d, lane, a)
+        out.append(list(a))
+    return out
+
+
+def read_patterns(d):
+    """(width in bytes, 64 byte addresses) of every read instruction of a tile
+    step: the plain reads (row blocks x k steps) and the transposing reads
+    (4 k steps of 16 rows x halves x head-dim blocks)."""
     nk, nd = d // 16, d // 32
-    for blk in range(2):  # plain: row 32 blk + lane % 32, chunk 2 ks + lane / 32
-        for ks in range(nk):
-            yield 16, [((32 * blk + (l & 31)) * d + ((2 * ks + (l >> 5)) ^ sw(l & 31)) * 8) * 2
-                       for l in range(64)]
-    for st in range(4):  # transposing: 4 rows x 2 chunks per 16 lanes
-        for ri in range(2):
-            for db in range(nd):
-                addrs = []
-                for l in range(64):
-                    row = 16 * st + 8 * ri + 4 * (l >> 5) + ((l & 15) >> 2)
-                    dd = 32 * db + 16 * ((l >> 4) & 1) + 4 * (l & 3)
-                    addrs.append((row * d + ((dd >> 3) ^ sw(row)) * 8 + (dd & 7)) * 2)
-                yield 8, addrs
+    plain = lane_offsets("shim_plain_offsets", d, 2 * nk)
+    for i in range(2 * nk):
+        yield 16, [2 * plain[l][i] for l in range(64)]
+    tr = lane_offsets("shim_tr_offsets", d, 2 * nd)
+    for st in range(4):
+        for i in range(2 * nd):
+            yield 8, [2 * (tr[l][i] + 16 * d * st) for l in range(64)]
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_backward_swizzle_is_a_permutation_and_conflict_free(d):
-    sw = swz(d)
+def test_swizzle_is_a_permutation_and_reads_are_conflict_free(d):
+    lib = host_shim.load()
     cpr = d // 8
     for row in range(64):
-        assert sorted(c ^ sw(row) for c in range(cpr)) == list(range(cpr))
+        assert sorted(c ^ lib.shim_swz_both(d, row) for c in range(cpr)) == list(range(cpr))
     for B in (128, 256):
-        for width, addrs in read_patterns(d, sw):
+        for width, addrs in read_patterns(d):
             assert conflicts(addrs, width, B) == 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_loads_place_what_the_reads_expect(d):
+    """Direct global->LDS loads put global chunk load_col(P) / 8 of row
+    load_row(P) at 16-byte position P; a plain read of that row and chunk
+    (plain_offsets' formula, row block 0, k step chunk / 2) lands on P."""
+    lib = host_shim.load()
+    cpr = d // 8
+    plain = lane_offsets("shim_plain_offsets", d, d // 8)
+    for P in range(64 * cpr):
+        row, chunk = lib.shim_load_row(d, P), lib.shim_load_col(d, P) // 8
+        if row >= 32:
+            continue
+        hl, ks = chunk % 2, chunk // 2
+        lane = row + 32 * hl
+        assert plain[lane][ks] == 8 * P, (P, row, chunk)
+
+
 def test_unswizzled_tiles_would_conflict():
-    # the model is not vacuous: without the swizzle both patterns conflict
+    # the model is not vacuous: without the swizzle the plain reads conflict
     for d in (64, 128):
-        total = sum(conflicts(a, w, 128) for w, a in read_patterns(d, lambda row: 0))
-        assert total > 0
+        addrs = [2 * ((l & 31) * d + (l >> 5) * 8) for l in range(64)]
+        assert conflicts(addrs, 16, 128) > 0

@@ -91,3 +91,51 @@ def test_local_head_instead_of_global_is_caught(monkeypatch):
     monkeypatch.setattr(O, "attention", attention_local_g)
     with pytest.raises(AssertionError):
         P.test_tensor_parallel_slice_equals_full_run()
+
+
+# ---- error-bound helpers (pins in tests/test_oracle_sensitivity.py) ----
+
+from tests import test_oracle_sensitivity as S  # noqa: E402
+
+_orig_dsens = O._d_sensitivity
+_orig_retained = O.retained_mask
+
+
+def _sensitivity_pins_fail():
+    for case in S.CASES:
+        for pin in (S.test_d_sensitivity_closed_form_for_uniform_rows,
+                    S.test_d_shift_bound_is_attained, S.test_d_shift_bound_holds_in_general):
+            try:
+                pin(case)
+            except AssertionError:
+                return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["double", "no_o_term", "no_abs_v"])
+def test_d_sensitivity_mutants_are_caught(kind, monkeypatch):
+    def mutant(P, v, o, do):
+        if kind == "double":
+            return 2.0 * _orig_dsens(P, v, o, do)
+        if kind == "no_o_term":
+            return (np.abs(do) * (P @ np.abs(v))).sum(axis=1)
+        return (np.abs(do) * (np.abs(P @ v) + np.abs(o))).sum(axis=1)
+    monkeypatch.setattr(O, "_d_sensitivity", mutant)
+    assert _sensitivity_pins_fail(), kind
+
+
+def test_retained_mask_prefix_or_is_caught(monkeypatch):
+    def prefix_or(n_max, g, p):
+        m = O.visible_mask(n_max, n_max, g, p)
+        earlier = np.logical_or.accumulate(m, axis=0)
+        return earlier & (np.arange(n_max)[None, :] <= np.arange(n_max)[:, None])
+    monkeypatch.setattr(O, "retained_mask", prefix_or)
+    with pytest.raises(AssertionError):
+        for case in S.RET_PATTERNS:
+            S.test_retained_mask_closed_form(case)
+
+
+def test_unmutated_helpers_pass():
+    assert not _sensitivity_pins_fail()
+    for case in S.RET_PATTERNS:
+        S.test_retained_mask_closed_form(case)
