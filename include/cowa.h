@@ -64,7 +64,8 @@ typedef enum {
   COWA_ERR_WORKSPACE = 3,     /* decode or backward workspace missing, misaligned or too small */
   COWA_ERR_PLAN_MISMATCH = 4, /* plan size does not match pattern/shape/tile */
   COWA_ERR_HIP = 5,           /* a HIP launch failed */
-  COWA_ERR_CAPACITY = 6       /* caller's plan buffers are too small */
+  COWA_ERR_CAPACITY = 6,      /* caller's plan buffers are too small */
+  COWA_ERR_SCRATCH_LIMIT = 7  /* needs more than the library's built-in scratch */
 } cowa_status;
 
 enum { COWA_MODE_COWA = 0, COWA_MODE_CAUSAL = 1, COWA_MODE_SINK_LOCAL = 2 };
@@ -215,6 +216,29 @@ cowa_status cowa_decode(const cowa_pattern* p, const void* q, const void* k_cach
                         int32_t B, int32_t H_q, int32_t H_kv_local, int32_t d, int32_t n_max,
                         const int64_t strides[10], float softmax_scale,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- cowa_decode_noalloc: cowa_decode without a workspace ---------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as cowa_decode, minus the workspace: the
+ * split partials live in a scratch array the library owns,
+ * COWA_DECODE_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends.  The call allocates and frees nothing; its
+ * first call on a device (with that device current) looks up the device's
+ * copy of the array.
+ *  COWA_ERR_SCRATCH_LIMIT when cowa_decode_workspace_size for the same
+ *  arguments exceeds COWA_DECODE_SCRATCH_BYTES (the 128K decode workload,
+ *  B = 16, H_q = 40, d = 128, needs 10.2 MB), checked before anything runs.
+ *  Every call on one GPU uses that GPU's single array: calls that overlap in
+ *  time on one GPU (different streams, or threads without ordering) race
+ *  and give wrong results; enqueue them on one stream. */
+#define COWA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+cowa_status cowa_decode_noalloc(const cowa_pattern* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* cache_seqlens,
+                                void* o, int32_t o_dtype, float* lse,
+                                int32_t B, int32_t H_q, int32_t H_kv_local, int32_t d,
+                                int32_t n_max, const int64_t strides[10],
+                                float softmax_scale, void* stream);
 
 /* ---- windowed KV cache for decode ---------------------------------------
  * Per-rank decode memory well below FullAttn's ("CoWindow Attention: Full

@@ -23,6 +23,8 @@ COWA_ERR_WORKSPACE = 3
 COWA_ERR_PLAN_MISMATCH = 4
 COWA_ERR_HIP = 5
 COWA_ERR_CAPACITY = 6
+COWA_ERR_SCRATCH_LIMIT = 7
+COWA_DECODE_SCRATCH_BYTES = 32 << 20
 COWA_MODE_COWA = 0
 COWA_MODE_CAUSAL = 1
 COWA_MODE_SINK_LOCAL = 2
@@ -34,7 +36,7 @@ EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
             "cowa_bwd_workspace_size", "cowa_bwd", "cowa_bwd_varlen", "cowa_kv_window_rows",
             "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window",
-            "cowa_fwd_varlen", "cowa_visible_ranges")
+            "cowa_fwd_varlen", "cowa_visible_ranges", "cowa_decode_noalloc")
 
 
 class CowaError(RuntimeError):
@@ -120,6 +122,9 @@ def load():
     lib.cowa_decode_window.restype = ctypes.c_int
     lib.cowa_decode_window.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                        P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_decode_noalloc.restype = ctypes.c_int
+    lib.cowa_decode_noalloc.argtypes = [pat, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                        i32, P(i64), f32, vp]
     lib.cowa_visible_ranges.restype = ctypes.c_int
     lib.cowa_visible_ranges.argtypes = [pat, i32, i32, P(i32), P(i32)]
     lib.cowa_fwd_varlen.restype = ctypes.c_int
@@ -266,6 +271,33 @@ def cowa_decode(p: cowa_pattern, q, k_cache, v_cache, cache_seqlens, o, lse,
                             float(softmax_scale), workspace.data_ptr(), workspace.numel()
                             * workspace.element_size(), _stream_ptr(stream))
     _check(st, "cowa_decode")
+
+
+def cowa_decode_noalloc(p: cowa_pattern, q, k_cache, v_cache, cache_seqlens, o, lse,
+                        softmax_scale: float, stream=None):
+    """cowa_decode with the library's own scratch (no workspace argument);
+    tensors as cowa_decode.  Marshalling only: allocates nothing."""
+    import torch
+    for t in (q, k_cache, v_cache):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q and caches must be bfloat16 GPU tensors")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise TypeError("cache_seqlens must be an int32 GPU tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    B, Hq, d = q.shape
+    _, n_max, Hkv, _ = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("caches must be [B, n_max, H_kv, d]")
+    if tuple(o.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("o must be [B, H_q, d] and lse [B, H_q]")
+    strides = (ctypes.c_int64 * 10)(*(_strides(q, 2) + _strides(k_cache, 3)
+                                      + _strides(v_cache, 3) + _strides(o, 2)))
+    st = load().cowa_decode_noalloc(ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), cache_seqlens.data_ptr(), o.data_ptr(),
+                                    _o_dtype(o), lse.data_ptr(), B, Hq, Hkv, d, n_max, strides,
+                                    float(softmax_scale), _stream_ptr(stream))
+    _check(st, "cowa_decode_noalloc")
 
 
 def cowa_bwd_block_sizes(d: int):

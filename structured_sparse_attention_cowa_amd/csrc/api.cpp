@@ -76,6 +76,7 @@ extern "C" const char* cowa_status_str(cowa_status s) {
     case COWA_ERR_PLAN_MISMATCH: return "plan does not match pattern, shape or tile";
     case COWA_ERR_HIP: return "HIP launch failed";
     case COWA_ERR_CAPACITY: return "plan buffers too small";
+    case COWA_ERR_SCRATCH_LIMIT: return "problem needs more than the library's decode scratch";
   }
   return "unknown status";
 }
@@ -364,7 +365,8 @@ static cowa_status decode_impl(const cowa_pattern* p, const void* q, const void*
                                int32_t o_dtype, float* lse, int32_t B, int32_t H_q,
                                int32_t H_kv_local, int32_t d, int32_t n_max,
                                const int64_t strides[10], float softmax_scale, void* workspace,
-                               size_t ws_bytes, void* stream, int win) {
+                               size_t ws_bytes, void* stream, int win,
+                               bool noalloc = false) {
   cowa_status st = validate_pattern(p, H_kv_local);
   if (st != COWA_OK) return st;
   if (!q || !k || !v || !cache_seqlens || !o || !lse || !strides) return COWA_ERR_INVALID_ARG;
@@ -379,6 +381,12 @@ static cowa_status decode_impl(const cowa_pattern* p, const void* q, const void*
   const DecodeGeometry geo = decode_geometry(p, B, H_q, H_kv_local, d, n_max);
   if ((int64_t)geo.n_splits > 0x7fffffffLL || B > 65535 || H_kv_local > 65535)
     return COWA_ERR_UNSUPPORTED;
+  if (noalloc) {
+    // the library's own scratch (cowa_decode_noalloc): no caller workspace
+    if (geo.total_bytes > COWA_DECODE_SCRATCH_BYTES) return COWA_ERR_SCRATCH_LIMIT;
+    if (decode_scratch_address(&workspace) != 0) return COWA_ERR_HIP;
+    ws_bytes = COWA_DECODE_SCRATCH_BYTES;
+  }
   if (!workspace || ws_bytes < geo.total_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return COWA_ERR_WORKSPACE;
 
@@ -423,6 +431,17 @@ extern "C" cowa_status cowa_decode(const cowa_pattern* p, const void* q, const v
                                    void* workspace, size_t ws_bytes, void* stream) {
   return decode_impl(p, q, k_cache, v_cache, cache_seqlens, o, o_dtype, lse, B, H_q, H_kv_local,
                      d, n_max, strides, softmax_scale, workspace, ws_bytes, stream, 0);
+}
+
+extern "C" cowa_status cowa_decode_noalloc(const cowa_pattern* p, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* cache_seqlens, void* o, int32_t o_dtype,
+                                           float* lse, int32_t B, int32_t H_q,
+                                           int32_t H_kv_local, int32_t d, int32_t n_max,
+                                           const int64_t strides[10], float softmax_scale,
+                                           void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, cache_seqlens, o, o_dtype, lse, B, H_q, H_kv_local,
+                     d, n_max, strides, softmax_scale, nullptr, 0, stream, 0, true);
 }
 
 // ---- windowed KV cache ----

@@ -170,6 +170,11 @@ struct BwdParams {
 int launch_fwd(const FwdParams& p, int d, int o_f32, void* stream);
 int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream);
 
+// The current device's address of the library-owned decode scratch
+// (COWA_DECODE_SCRATCH_BYTES, 256-byte aligned): looked up once per device.
+// Returns a hipError_t value (0 on success).
+int decode_scratch_address(void** ptr);
+
 // Windowed KV cache (fill from a full cache / append one token).
 struct KvWinParams {
   const uint16_t* k_src;  // fill: full cache [B, n_max, H_kv, d]; append: [B, H_kv, d]

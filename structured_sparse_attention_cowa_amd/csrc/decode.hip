@@ -20,6 +20,8 @@
 // by their log-sum-exp, weights staged in LDS, partial loads all in flight.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "cowa_internal.h"
 
 namespace cowa {
@@ -510,6 +512,35 @@ int launch_decode(const DecodeParams& p, int d, int o_f32, void* stream) {
   int bad = d == 128 ? dispatch_group<128>(p, s) : dispatch_group<64>(p, s);
   if (bad) return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+// Scratch of cowa_decode_noalloc: the split kernel's partial outputs and
+// log-sum-exps, for callers that cannot allocate.  Every GPU holds its own
+// copy at its own address; host code must use the address looked up below,
+// never the symbol itself (in host code the symbol is only a stand-in).
+static __device__ __align__(256) unsigned char scratch[COWA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int decode_scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 }  // namespace cowa

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     assert C.cowa_status_str(0) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert C.cowa_status_str(s) != "unknown status"
 
 
@@ -217,6 +217,28 @@ def test_decode_host_validation(lib):
     assert call(nmax=0) == C.COWA_ERR_INVALID_ARG
     assert call(B=0) == C.COWA_ERR_INVALID_ARG
     assert call(Hq=0) == C.COWA_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_host_validation(lib):
+    """cowa_decode_noalloc checks its arguments, and that the problem fits the
+    library's scratch, before it touches a device (fake pointers, no GPU)."""
+    cp, _ = pat(n_ctx=131072, sink=128, window=8192, h_kv_global=8)
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(B=16, Hq=40, Hkv=8, d=128, nmax=131072, scale=0.1, o_dtype=0):
+        arr = (ctypes.c_int64 * 10)(*([1] * 10))
+        return lib.cowa_decode_noalloc(ctypes.byref(cp), fake, fake, fake, fake, fake, o_dtype,
+                                       fake, B, Hq, Hkv, d, nmax, arr, scale, None)
+
+    # the 128K decode workload fits; 64 sequences of it do not
+    assert C.cowa_decode_workspace_size(cp, 16, 40, 8, 128, 131072) <= C.COWA_DECODE_SCRATCH_BYTES
+    assert C.cowa_decode_workspace_size(cp, 64, 40, 8, 128, 131072) > C.COWA_DECODE_SCRATCH_BYTES
+    assert call(B=64) == C.COWA_ERR_SCRATCH_LIMIT
+    assert call(d=80) == C.COWA_ERR_UNSUPPORTED
+    assert call(Hq=6) == C.COWA_ERR_INVALID_ARG
+    assert call(B=0) == C.COWA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == C.COWA_ERR_INVALID_ARG
+    assert call(o_dtype=2) == C.COWA_ERR_INVALID_ARG
 
 
 def test_single_hip_runtime_after_load(lib):
