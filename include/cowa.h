@@ -44,6 +44,13 @@
  *    empty (cu_seqlens[b+1] == cu_seqlens[b]); it produces no rows.
  *  - bf16 means IEEE bfloat16 stored as 2 bytes.  Strides are in elements;
  *    the last (head-dim) axis is always contiguous.
+ *  - Alignment: the kernels move 16 bytes per lane at the start of every
+ *    row, so every tensor base pointer (q, k, v, o, dO, dq, dk, dv, caches,
+ *    windowed caches, new tokens) must be 16-byte aligned and every batch,
+ *    token and head stride a multiple of 16 bytes (8 bf16 or 4 fp32
+ *    elements); otherwise COWA_ERR_INVALID_ARG before any launch.  The
+ *    forward also needs 64 token strides of K and of V below 2^30 elements
+ *    (COWA_ERR_UNSUPPORTED otherwise).
  *  - The library is thread-safe.  Its only state is per-thread caches of
  *    plan sizes and launch-order choices per shape, which change no result.
  */

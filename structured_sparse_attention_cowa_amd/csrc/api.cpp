@@ -248,6 +248,17 @@ static bool strides_ok(const int64_t* s, int n) {
   return true;
 }
 
+// The kernels move 16 bytes per lane from and to the start of every row: a
+// tensor's base pointer must be 16-byte aligned and its n row strides
+// (elements of elem_bytes each) multiples of 16 bytes.
+static bool rows16(const void* base, const int64_t* strides, int n, int elem_bytes) {
+  if (reinterpret_cast<uintptr_t>(base) & 15) return false;
+  const int64_t m = 16 / elem_bytes;
+  for (int i = 0; i < n; ++i)
+    if (strides[i] % m) return false;
+  return true;
+}
+
 // Prefill forward, batched (cu_seqlens NULL: [B, N, ...] with b strides) or
 // packed (cu_seqlens: B sequences of length <= N at rows cu_seqlens[b]..).
 static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, const int32_t* d_col,
@@ -265,10 +276,13 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
   if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 12)) return COWA_ERR_INVALID_ARG;
+  if (!rows16(q, strides, 3, 2) || !rows16(k, strides + 3, 3, 2) || !rows16(v, strides + 6, 3, 2) ||
+      !rows16(o, strides + 9, 3, o_dtype == COWA_DTYPE_F32 ? 4 : 2))
+    return COWA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (block_m != kFwdBlockM || block_n != kFwdBlockN) return COWA_ERR_UNSUPPORTED;
-  // per-lane offsets inside one K/V tile are 32-bit
-  if ((int64_t)block_n * strides[4] >= (1LL << 31) || (int64_t)block_n * strides[7] >= (1LL << 31))
+  // per-lane byte offsets inside one K/V tile are 31-bit (buffer loads)
+  if ((int64_t)block_n * strides[4] >= (1LL << 30) || (int64_t)block_n * strides[7] >= (1LL << 30))
     return COWA_ERR_UNSUPPORTED;
   const int64_t nqt = (N + block_m - 1) / block_m;
   if (!grid_fits((int64_t)B * nqt * H_q, (int64_t)B * H_q)) return COWA_ERR_UNSUPPORTED;
@@ -374,6 +388,8 @@ static cowa_status decode_impl(const cowa_pattern* p, const void* q, const void*
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return COWA_ERR_INVALID_ARG;
   if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 10)) return COWA_ERR_INVALID_ARG;
+  if (!rows16(q, strides, 2, 2) || !rows16(k, strides + 2, 3, 2) || !rows16(v, strides + 5, 3, 2))
+    return COWA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (win && p->mode == COWA_MODE_CAUSAL) return COWA_ERR_UNSUPPORTED;
   const int32_t G = H_q / H_kv_local;
@@ -508,6 +524,9 @@ extern "C" cowa_status cowa_kv_window_fill(const cowa_pattern* p, const void* k_
   if (!k_cache || !v_cache || !cache_seqlens || !k_win || !v_win || !strides)
     return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 8)) return COWA_ERR_INVALID_ARG;
+  if (!rows16(k_cache, strides, 3, 2) || !rows16(v_cache, strides + 3, 3, 2) ||
+      !rows16(k_win, strides + 6, 1, 2) || !rows16(v_win, strides + 7, 1, 2))
+    return COWA_ERR_INVALID_ARG;
   KvWinParams kp;
   int32_t max_rows = 0;
   cowa_status st = kvwin_common(p, B, H_kv_local, d, n_max, strides + 6, &kp, &max_rows);
@@ -531,6 +550,9 @@ extern "C" cowa_status cowa_kv_window_append(const cowa_pattern* p, const void* 
   if (!k_new || !v_new || !cache_seqlens || !k_win || !v_win || !strides)
     return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 6)) return COWA_ERR_INVALID_ARG;
+  if (!rows16(k_new, strides, 2, 2) || !rows16(v_new, strides + 2, 2, 2) ||
+      !rows16(k_win, strides + 4, 1, 2) || !rows16(v_win, strides + 5, 1, 2))
+    return COWA_ERR_INVALID_ARG;
   KvWinParams kp;
   cowa_status st = kvwin_common(p, B, H_kv_local, d, n_max, strides + 4, &kp, nullptr);
   if (st != COWA_OK) return st;
@@ -643,6 +665,13 @@ static cowa_status bwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr,
   if (o_dtype != COWA_DTYPE_BF16 && o_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (g_dtype != COWA_DTYPE_BF16 && g_dtype != COWA_DTYPE_F32) return COWA_ERR_INVALID_ARG;
   if (!strides_ok(strides, 24)) return COWA_ERR_INVALID_ARG;
+  {
+    const int ob = o_dtype == COWA_DTYPE_F32 ? 4 : 2, gb = g_dtype == COWA_DTYPE_F32 ? 4 : 2;
+    const void* bases[8] = {q, k, v, o, dout, dq, dk, dv};
+    const int bytes[8] = {2, 2, 2, ob, 2, gb, gb, gb};
+    for (int i = 0; i < 8; ++i)
+      if (!rows16(bases[i], strides + 3 * i, 3, bytes[i])) return COWA_ERR_INVALID_ARG;
+  }
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (block_m != kFwdBlockM || block_n != kFwdBlockN || block_m_kv != kBwdBlockM ||
       block_n_kv != kBwdBlockN)

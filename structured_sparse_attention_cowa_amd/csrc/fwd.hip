@@ -156,22 +156,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_kcol[i];
     ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_vcol[i];
   }
-  // Loads of one K (or V) tile into LDS buffer dst.  Keys past N (ragged last
-  // tile) are clamped to N - 1: they only occur in tiles the plan marks
-  // partial, where they are masked (probability exactly 0).
+  // Loads of one K (or V) tile into LDS buffer dst, through a buffer
+  // resource based at the tile (buffer_load ... lds).  Keys past N (ragged
+  // last tile) are clamped to N - 1: they only occur in tiles the plan marks
+  // partial, where they are masked (probability exactly 0).  The buffer form
+  // of the direct-to-LDS load (not the global one) lets the compiler count
+  // the LDS reads that feed the MFMAs precisely while tile loads are in
+  // flight; with the global form it waits for every outstanding LDS read at
+  // each of them.  Byte offsets inside a tile stay below 2^31 (checked on the
+  // host).
   auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, const int* col,
                        int kj, uint16_t* dst) {
     const int key0 = kj * BN;
+    const uint16_t* t = base + (int64_t)key0 * stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(t), (short)0, 0x7fffffff, 0x00020000);
     if (key0 + BN <= N) {
-      const uint16_t* t = base + (int64_t)key0 * stride;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) g2lds16(t + off[i], dst + (wave * LOADS + i) * 512);
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * LOADS + i) * 512),
+                                                 16, off[i] * 2, 0, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
         key = key < N ? key : N - 1;
-        g2lds16(base + (int64_t)key * stride + col[i], dst + (wave * LOADS + i) * 512);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(dst + (wave * LOADS + i) * 512), 16,
+            (int)(((int64_t)(key - key0) * stride + col[i]) * 2), 0, 0, 0);
       }
     }
   };

@@ -68,7 +68,7 @@ def test_window_validation(lib):
     small = (ctypes.c_int64 * 8)(1, 1, 1, 1, 1, 1, total * 128 - 1, total * 128)
     assert L.cowa_kv_window_fill(ctypes.byref(cp), fake, fake, fake, fake, fake, 2, 4, 128, 1000,
                                  small, None) == C.COWA_ERR_INVALID_ARG
-    st = (ctypes.c_int64 * 6)(1, 1, 1, 1, total * 128, total * 128)
+    st = (ctypes.c_int64 * 6)(8, 8, 8, 8, total * 128, total * 128)
     assert L.cowa_kv_window_append(ctypes.byref(cp), fake, fake, fake, fake, fake, 2, 4, 96,
                                    1000, st, None) == C.COWA_ERR_UNSUPPORTED
     dst = (ctypes.c_int64 * 6)(1, 1, total * 128 - 8, total * 128, 1, 1)

@@ -156,7 +156,7 @@ def _fwd_raw(lib, cp, nnz=None, bm=None, bn=None, B=1, N=256, Hq=4, Hkv=2, d=128
     bn = fbn if bn is None else bn
     if nnz is None:
         nnz = C.cowa_plan_size(cp, N, Hkv, fbm, fbn)
-    s = strides if strides is not None else [1] * 12
+    s = strides if strides is not None else [8] * 12
     arr = (ctypes.c_int64 * 12)(*s)
     return lib.cowa_fwd(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, bm, bn,
                         ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], o_dtype, ptrs["lse"],
@@ -174,7 +174,15 @@ def test_fwd_host_validation(lib):
     assert _fwd_raw(lib, cp, scale=0.0) == E.COWA_ERR_INVALID_ARG
     assert _fwd_raw(lib, cp, scale=float("nan")) == E.COWA_ERR_INVALID_ARG
     assert _fwd_raw(lib, cp, o_dtype=7) == E.COWA_ERR_INVALID_ARG
-    assert _fwd_raw(lib, cp, strides=[-1] + [1] * 11) == E.COWA_ERR_INVALID_ARG
+    assert _fwd_raw(lib, cp, strides=[-1] + [8] * 11) == E.COWA_ERR_INVALID_ARG
+    # 16-byte rows: bf16 strides must be multiples of 8, fp32 O strides of 4
+    for i in range(9):
+        assert _fwd_raw(lib, cp, strides=[8] * i + [4] + [8] * (11 - i)) == \
+            E.COWA_ERR_INVALID_ARG, i
+    # fp32 O with 4-element strides passes the alignment check (and reaches
+    # the plan check)
+    assert _fwd_raw(lib, cp, strides=[8] * 9 + [4] * 3, o_dtype=1, nnz=3) == \
+        E.COWA_ERR_PLAN_MISMATCH
     for nm in ("rp", "col", "fl", "q", "k", "v", "o", "lse"):
         assert _fwd_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
     # empty inputs are rejected before anything runs
@@ -192,6 +200,29 @@ def test_fwd_host_validation(lib):
     assert _fwd_raw(lib, cp4, nnz=nnz_other, N=4096) == E.COWA_ERR_PLAN_MISMATCH
 
 
+def test_misaligned_pointers_are_rejected(lib):
+    """A base pointer off a 16-byte boundary is refused before any launch."""
+    cp, _ = pat(n_ctx=256, h_kv_global=2)
+    fbm, fbn = C.cowa_fwd_block_sizes(128)
+    nnz = C.cowa_plan_size(cp, 256, 2, fbm, fbn)
+    good, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    arr = (ctypes.c_int64 * 12)(*([8] * 12))
+    for which in range(4):  # q, k, v, o
+        t = [good] * 4
+        t[which] = bad
+        assert lib.cowa_fwd(ctypes.byref(cp), good, good, good, nnz, fbm, fbn, *t, 0, good, 1, 256,
+                            4, 2, 128, arr, 0.1, None) == C.COWA_ERR_INVALID_ARG, which
+    cpd, _ = pat(n_ctx=4096, sink=16, window=128, h_kv_global=4)
+    ws = C.cowa_decode_workspace_size(cpd, 2, 8, 4, 128, 4096)
+    arr10 = (ctypes.c_int64 * 10)(*([8] * 10))
+    for which in range(3):  # q, k, v
+        t = [good] * 3
+        t[which] = bad
+        assert lib.cowa_decode(ctypes.byref(cpd), *t, good, good, 0, good, 2, 8, 4, 128, 4096,
+                               arr10, 0.1, ctypes.c_void_p(0x100000), ws, None) == \
+            C.COWA_ERR_INVALID_ARG, which
+
+
 def test_decode_host_validation(lib):
     cp, _ = pat(n_ctx=4096, sink=16, window=128, h_kv_global=4)
     ws = C.cowa_decode_workspace_size(cp, 2, 8, 4, 128, 4096)
@@ -200,7 +231,7 @@ def test_decode_host_validation(lib):
 
     def call(B=2, Hq=8, Hkv=4, d=128, nmax=4096, ws_ptr=ctypes.c_void_p(0x100000),
              ws_bytes=ws, o_dtype=0, scale=0.1, p=cp):
-        arr = (ctypes.c_int64 * 10)(*([1] * 10))
+        arr = (ctypes.c_int64 * 10)(*([8] * 10))
         return lib.cowa_decode(ctypes.byref(p), fake, fake, fake, fake, fake, o_dtype, fake, B,
                                Hq, Hkv, d, nmax, arr, scale, ws_ptr, ws_bytes, None)
 
@@ -226,7 +257,7 @@ def test_decode_noalloc_host_validation(lib):
     fake = ctypes.c_void_p(0x1000)
 
     def call(B=16, Hq=40, Hkv=8, d=128, nmax=131072, scale=0.1, o_dtype=0):
-        arr = (ctypes.c_int64 * 10)(*([1] * 10))
+        arr = (ctypes.c_int64 * 10)(*([8] * 10))
         return lib.cowa_decode_noalloc(ctypes.byref(cp), fake, fake, fake, fake, fake, o_dtype,
                                        fake, B, Hq, Hkv, d, nmax, arr, scale, None)
 
@@ -259,7 +290,7 @@ def _varlen_raw(lib, cp, nnz=None, n_seqs=3, max_seqlen=300, total=700, Hq=4, Hk
     fbm, fbn = C.cowa_fwd_block_sizes(128)
     if nnz is None:
         nnz = C.cowa_plan_size(cp, max(max_seqlen, 1), Hkv, fbm, fbn)
-    arr = (ctypes.c_int64 * 8)(*(strides if strides is not None else [1] * 8))
+    arr = (ctypes.c_int64 * 8)(*(strides if strides is not None else [8] * 8))
     return lib.cowa_fwd_varlen(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, fbm,
                                fbn, ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], 1, ptrs["lse"],
                                ptrs["cu"], n_seqs, max_seqlen, total, Hq, Hkv, d, arr, scale,
@@ -275,7 +306,8 @@ def test_fwd_varlen_host_validation(lib):
     assert _varlen_raw(lib, cp, Hq=3) == E.COWA_ERR_INVALID_ARG
     assert _varlen_raw(lib, cp, d=96) == E.COWA_ERR_UNSUPPORTED
     assert _varlen_raw(lib, cp, scale=-1.0) == E.COWA_ERR_INVALID_ARG
-    assert _varlen_raw(lib, cp, strides=[1] * 7 + [-1]) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, strides=[8] * 7 + [-1]) == E.COWA_ERR_INVALID_ARG
+    assert _varlen_raw(lib, cp, strides=[8, 12] + [8] * 6) == E.COWA_ERR_INVALID_ARG
     for nm in ("rp", "col", "fl", "q", "k", "v", "o", "lse", "cu"):
         assert _varlen_raw(lib, cp, null=nm) == E.COWA_ERR_INVALID_ARG, nm
     # the plan must be the one for max_seqlen
