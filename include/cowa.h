@@ -8,10 +8,11 @@
  * GQA attention in which every KV head sees a shared prefix-sink window and a
  * shared near-diagonal window, while the rest of the causal history is split
  * into non-overlapping long-range intervals, one per KV head, so that the
- * union over heads covers the whole causal prefix.  Each head applies softmax
- * over its own visible set only (same news page, paragraph on what CoWA does
- * not claim).  The pattern is computed from positions and the global KV-head
- * index alone (news page, efficiency and tensor-parallelism paragraphs).
+ * union over heads covers the whole causal prefix.  A head's softmax
+ * normalises over the keys that head sees and no others (same news page,
+ * paragraph on what CoWA does not claim).  The pattern is computed from
+ * positions and the global KV-head index alone (news page, efficiency and
+ * tensor-parallelism paragraphs).
  *
  * The pages give no formula; this library fixes the band partition as:
  *     L = ceil((n_ctx - W) / h_kv_global)   if n_ctx > W, else L = 0
@@ -157,6 +158,10 @@ cowa_status cowa_plan(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
  *  plan        d_row_ptr/d_col/d_flags: device copies of cowa_plan's output
  *              for (p, N, H_kv_local, block_m, block_n); nnz its length.
  *              COWA_ERR_PLAN_MISMATCH if nnz differs from cowa_plan_size.
+ *              That length is the only check (the plan is on the device and
+ *              the library never reads it back): a plan built for other
+ *              arguments with the same length, or altered after cowa_plan,
+ *              gives undefined results.
  *  q           bf16 [B, N, H_q, d] with element strides strides[0..2] (b,t,h)
  *  k, v        bf16 [B, N, H_kv_local, d], strides[3..5] and strides[6..8]
  *  o           [B, N, H_q, d] of o_dtype (COWA_DTYPE_BF16 or _F32),

@@ -118,19 +118,16 @@ def _decode_full():
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-def test_decode_128k_workload_sampled(lib, mode):
-    """Full 128K decode workload (B=16, H_q=40, H_kv=8); every query head of a
-    seeded sample of sequences is checked against the oracle."""
+def test_decode_128k_workload(lib, mode):
+    """Full 128K decode workload (B=16, H_q=40, H_kv=8): every query head of
+    every sequence is checked against the oracle."""
     import torch
     w, lens, q_bits, k, v = _decode_full()
     print(f"[decode] 128K workload mode={mode} lens={list(lens)}", flush=True)
     o, lse = run_decode(q_bits, k, v, lens, w.sink, w.window, w.h_kv_global, w.n_ctx, mode=mode)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    rng = np.random.Generator(np.random.PCG64(77 + mode))
-    bs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
-                    list(rng.choice(w.B, 2, replace=False))))
     p = O.Pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, mode)
-    for b in bs:
+    for b in range(w.B):
         L = int(lens[b])
         kb = k[b:b + 1, :L].float().cpu().numpy()
         vb = v[b:b + 1, :L].float().cpu().numpy()
