@@ -676,10 +676,10 @@ static cowa_status bwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr,
   if (block_m != kFwdBlockM || block_n != kFwdBlockN || block_m_kv != kBwdBlockM ||
       block_n_kv != kBwdBlockN)
     return COWA_ERR_UNSUPPORTED;
-  // per-lane offsets inside one 64-row tile are 32-bit
+  // per-lane byte offsets inside one 64-row tile are 31-bit (buffer loads)
   const int tile_strides[4] = {1, 4, 7, 13};  // q, k, v, dout row strides
   for (int i : tile_strides)
-    if ((int64_t)64 * strides[i] >= (1LL << 31)) return COWA_ERR_UNSUPPORTED;
+    if ((int64_t)64 * strides[i] >= (1LL << 30)) return COWA_ERR_UNSUPPORTED;
   const int64_t nqt = (N + block_m - 1) / block_m;
   const int64_t nkt_kv = (N + block_n_kv - 1) / block_n_kv;
   if (!grid_fits((int64_t)B * nqt * H_q, H_q) ||

@@ -222,8 +222,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   const uint16_t* vbase =
       p.v + (int64_t)b * p.vs_b + (int64_t)sp.start * p.vs_t + (int64_t)h * p.vs_h;
 
-  // lane offsets inside a tile are unsigned 32-bit (the host bounds 64 rows x
-  // stride below 2^31), so the loads use a uniform 64-bit base plus a 32-bit offset
+  // lane offsets inside a tile are 32-bit (the host bounds 64 rows x stride
+  // below 2^30 elements, so byte offsets stay below 2^31): the loads use a
+  // buffer resource at the tile plus a 32-bit byte offset
   int ld_row[LOADS], ld_col[LOADS];
   uint32_t ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
@@ -238,21 +239,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QTHREADS, QTHREADS),
   // tiles the plan marks partial, where they are masked) are clamped.
   auto load_kv = [&](int kj, uint16_t* kd, uint16_t* vd) {
     const int key0 = kj * QBN;
+    const __amdgpu_buffer_rsrc_t kr = lds_rsrc(kbase + (int64_t)key0 * p.ks_t);
+    const __amdgpu_buffer_rsrc_t vr = lds_rsrc(vbase + (int64_t)key0 * p.vs_t);
     if (key0 + QBN <= sp.n) {
-      const uint16_t* kt = kbase + (int64_t)key0 * p.ks_t;
-      const uint16_t* vt = vbase + (int64_t)key0 * p.vs_t;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        g2lds16(kt + ld_koff[i], kd + (wave * LOADS + i) * 512);
-        g2lds16(vt + ld_voff[i], vd + (wave * LOADS + i) * 512);
+        buf2lds16(kr, (int)(ld_koff[i] * 2), kd + (wave * LOADS + i) * 512);
+        buf2lds16(vr, (int)(ld_voff[i] * 2), vd + (wave * LOADS + i) * 512);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
         key = key < sp.n ? key : sp.n - 1;
-        g2lds16(kbase + (int64_t)key * p.ks_t + ld_col[i], kd + (wave * LOADS + i) * 512);
-        g2lds16(vbase + (int64_t)key * p.vs_t + ld_col[i], vd + (wave * LOADS + i) * 512);
+        buf2lds16(kr, (int)(((key - key0) * p.ks_t + ld_col[i]) * 2),
+                  kd + (wave * LOADS + i) * 512);
+        buf2lds16(vr, (int)(((key - key0) * p.vs_t + ld_col[i]) * 2),
+                  vd + (wave * LOADS + i) * 512);
       }
     }
   };
@@ -503,26 +506,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KTHREADS, KTHREADS),
         p.q + (int64_t)b * p.qs_b + (int64_t)sp.start * p.qs_t + (int64_t)hq * p.qs_h;
     const uint16_t* ob =
         p.dout + (int64_t)b * p.dos_b + (int64_t)sp.start * p.dos_t + (int64_t)hq * p.dos_h;
+    const __amdgpu_buffer_rsrc_t qr = lds_rsrc(qb + (int64_t)r0 * p.qs_t);
+    const __amdgpu_buffer_rsrc_t orr = lds_rsrc(ob + (int64_t)r0 * p.dos_t);
     if (r0 + KBM <= sp.n) {
-      const uint16_t* qt = qb + (int64_t)r0 * p.qs_t;
-      const uint16_t* ot = ob + (int64_t)r0 * p.dos_t;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        g2lds16(qt + ld_qoff[i], qd + (wave * LOADS + i) * 512);
-        g2lds16(ot + ld_ooff[i], od + (wave * LOADS + i) * 512);
+        buf2lds16(qr, (int)(ld_qoff[i] * 2), qd + (wave * LOADS + i) * 512);
+        buf2lds16(orr, (int)(ld_ooff[i] * 2), od + (wave * LOADS + i) * 512);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int t = r0 + ld_row[i];
         t = t < sp.n ? t : sp.n - 1;
-        g2lds16(qb + (int64_t)t * p.qs_t + ld_col[i], qd + (wave * LOADS + i) * 512);
-        g2lds16(ob + (int64_t)t * p.dos_t + ld_col[i], od + (wave * LOADS + i) * 512);
+        buf2lds16(qr, (int)(((t - r0) * p.qs_t + ld_col[i]) * 2), qd + (wave * LOADS + i) * 512);
+        buf2lds16(orr, (int)(((t - r0) * p.dos_t + ld_col[i]) * 2),
+                  od + (wave * LOADS + i) * 512);
       }
     }
     const int64_t so = ((int64_t)b * p.Hq + hq) * p.npad + r0;
-    if (wave == 0) g2lds4(p.lse2 + so + lane, sdst);
-    if (wave == 1) g2lds4(p.delta + so + lane, sdst + KBM);
+    if (wave == 0) buf2lds4(lds_rsrc(p.lse2 + so), lane * 4, sdst);
+    if (wave == 1) buf2lds4(lds_rsrc(p.delta + so), lane * 4, sdst + KBM);
   };
 
   int n_off[2][NK], t_off[2][ND];

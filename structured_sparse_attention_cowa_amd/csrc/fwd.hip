@@ -168,22 +168,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, const int* col,
                        int kj, uint16_t* dst) {
     const int key0 = kj * BN;
-    const uint16_t* t = base + (int64_t)key0 * stride;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(t), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = lds_rsrc(base + (int64_t)key0 * stride);
     if (key0 + BN <= N) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * LOADS + i) * 512),
-                                                 16, off[i] * 2, 0, 0, 0);
+      for (int i = 0; i < LOADS; ++i) buf2lds16(rs, off[i] * 2, dst + (wave * LOADS + i) * 512);
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row[i];
         key = key < N ? key : N - 1;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(dst + (wave * LOADS + i) * 512), 16,
-            (int)(((int64_t)(key - key0) * stride + col[i]) * 2), 0, 0, 0);
+        buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + col[i]) * 2),
+                  dst + (wave * LOADS + i) * 512);
       }
     }
   };

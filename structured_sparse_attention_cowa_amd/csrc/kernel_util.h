@@ -67,15 +67,26 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, r);
 }
 
-// One 16-byte chunk per lane from global memory straight into LDS; the
-// wavefront's 64 chunks land contiguously at lds_base (+16 bytes per lane).
-__device__ __forceinline__ void g2lds16(const uint16_t* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)lds_base, 16, 0, 0);
+// Direct global -> LDS loads go through a buffer resource (buffer_load ...
+// lds) rather than the FLAT-encoded global_load_lds: with a FLAT load to LDS
+// in flight the compiler's wait-count pass cannot count LDS reads precisely
+// and waits for every outstanding one before each use.  A resource covers
+// 2^31 - 1 bytes from its base; callers keep byte offsets below that.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lds_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
 }
 
-// One dword per lane into LDS at lds_base + 4 * lane.
-__device__ __forceinline__ void g2lds4(const float* g, float* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)lds_base, 4, 0, 0);
+// One 16-byte chunk per lane at byte offset voff from the resource's base
+// into LDS; the wavefront's 64 chunks land contiguously at lds_base
+// (+16 bytes per lane).
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, int voff, uint16_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// One dword per lane at byte offset voff into LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t rs, int voff, float* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 4, voff, 0, 0, 0);
 }
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
