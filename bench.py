@@ -49,7 +49,8 @@ def visible_counts(t, g, sink, window, band):
 # headers every kernel source includes: a change to any of them, or to the
 # kernel source itself, invalidates the counters recorded for that kernel
 KERNEL_HEADERS = tuple(f"structured_sparse_attention_cowa_amd/csrc/{h}"
-                       for h in ("cowa_internal.h", "cowa_pattern.h", "kernel_util.h"))
+                       for h in ("cowa_internal.h", "cowa_pattern.h", "kernel_util.h",
+                                  "cowa_layout.h"))
 
 
 def source_digest(source: str) -> str:
