@@ -146,15 +146,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
   // holds row P / CPR, column chunk (P % CPR) ^ swizzle(row).  Per-lane
   // offsets inside a tile are fixed; the tile base is uniform.
-  int ld_row[LOADS], ld_kcol[LOADS], ld_vcol[LOADS], ld_koff[LOADS], ld_voff[LOADS];
+  auto ld_row = [&](int i) { return ((wave * LOADS + i) * 64 + lane) / CPR; };
+  auto ld_col = [&](int i, bool is_v) {
+    const int r = ld_row(i);
+    return ((lane % CPR) ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 8;
+  };
+  int ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int P = (wave * LOADS + i) * 64 + lane;
-    ld_row[i] = P / CPR;
-    ld_kcol[i] = ((P % CPR) ^ kswz<D>(ld_row[i])) * 8;
-    ld_vcol[i] = ((P % CPR) ^ vswz<D>(ld_row[i])) * 8;
-    ld_koff[i] = (int)(ld_row[i] * p.ks_t) + ld_kcol[i];
-    ld_voff[i] = (int)(ld_row[i] * p.vs_t) + ld_vcol[i];
+    ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i, false);
+    ld_voff[i] = (int)(ld_row(i) * p.vs_t) + ld_col(i, true);
   }
   // Loads of one K (or V) tile into LDS buffer dst, through a buffer
   // resource based at the tile (buffer_load ... lds).  Keys past N (ragged
@@ -165,8 +166,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   // flight; with the global form it waits for every outstanding LDS read at
   // each of them.  Byte offsets inside a tile stay below 2^31 (checked on the
   // host).
-  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, const int* col,
-                       int kj, uint16_t* dst) {
+  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, bool is_v, int kj,
+                       uint16_t* dst) {
     const int key0 = kj * BN;
     const __amdgpu_buffer_rsrc_t rs = lds_rsrc(base + (int64_t)key0 * stride);
     if (key0 + BN <= N) {
@@ -175,26 +176,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        int key = key0 + ld_row[i];
+        int key = key0 + ld_row(i);
         key = key < N ? key : N - 1;
-        buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + col[i]) * 2),
+        buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + ld_col(i, is_v)) * 2),
                   dst + (wave * LOADS + i) * 512);
       }
     }
   };
 
-  // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl
+  // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl.
+  // At d = 128 the swizzle repeats every 16 rows, so block 1 reads 32 rows
+  // (a constant) further and only block 0's offsets occupy registers.
   int k_off[2][NK];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
-      k_off[blk][ks] = (32 * blk + l32) * D + (((2 * ks + hl) ^ kswz<D>(32 * blk + l32)) * 8);
+      k_off[blk][ks] = (blk == 1 && D == 128)
+                           ? k_off[0][ks] + 32 * D
+                           : (32 * blk + l32) * D + (((2 * ks + hl) ^ kswz<D>(32 * blk + l32)) * 8);
   // V transposed-read offsets (second product, A operand): for 16-key step st,
   // d block db and half ri, lane reads key 16*st + 8*ri + 4*hl + (lane&15)/4 at
   // dims 32*db + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
   const int r16 = lane & 15;
   const int gi = (lane >> 4) & 1;
+  // (the swizzle depends on key mod 4, so half ri = 1 is 8 rows further)
   int v_off[2][ND];
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri)
@@ -202,7 +208,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     for (int db = 0; db < ND; ++db) {
       const int key = 8 * ri + 4 * hl + (r16 >> 2);
       const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
-      v_off[ri][db] = key * D + (((d >> 3) ^ vswz<D>(key)) * 8) + (d & 7);
+      v_off[ri][db] = ri == 1 ? v_off[0][db] + 8 * D
+                              : key * D + (((d >> 3) ^ vswz<D>(key)) * 8) + (d & 7);
     }
 
   // Plan entries travel 64 at a time, one per lane (tile index with the
@@ -239,9 +246,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   if (e0 < e1) {
     c_cur = entry(e0);
     c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
-    load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_cur & 0x7fffffff, K0);
-    load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_cur & 0x7fffffff, V0);
-    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n1 & 0x7fffffff, K1);
+    load_tile(kbase, p.ks_t, ld_koff, false, c_cur & 0x7fffffff, K0);
+    load_tile(vbase, p.vs_t, ld_voff, true, c_cur & 0x7fffffff, V0);
+    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, false, c_n1 & 0x7fffffff, K1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(K0, s_first);
@@ -264,11 +271,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pchunk = plan_chunk(pbase);
       }
       c_n2 = entry(e + 2);
-      load_tile(kbase, p.ks_t, ld_koff, ld_kcol, c_n2 & 0x7fffffff, Kw);
+      load_tile(kbase, p.ks_t, ld_koff, false, c_n2 & 0x7fffffff, Kw);
     }
-    if (has_next) load_tile(vbase, p.vs_t, ld_voff, ld_vcol, c_n1 & 0x7fffffff, Vw);
+    if (has_next) load_tile(vbase, p.vs_t, ld_voff, true, c_n1 & 0x7fffffff, Vw);
 
-    if (!full) {
+    if (__builtin_expect(!full, 0)) {
       // register i of block blk holds key kj*64 + 4 hl + o
       const uint64_t vis = row_visible_bits(hp, q_row, kj * BN + 4 * hl);
 #pragma unroll
