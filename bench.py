@@ -135,9 +135,11 @@ def main():
     plan0 = make_plan(0) if need_prefill else None
     plan_ms = (time.perf_counter() - t_plan0) * 1e3
 
+    fws = torch.empty(C.cowa_fwd_workspace_size(B, N, Hkv, d), dtype=torch.uint8, device=dev)
+
     def prefill(plan):
         p, rp, col, fl, nnz = plan
-        C.cowa_fwd(p, rp, col, fl, nnz, bm, bn, q, k, v, o, lse, scale)
+        C.cowa_fwd(p, rp, col, fl, nnz, bm, bn, q, k, v, o, lse, scale, workspace=fws)
 
     # ---------------- backward setup (same prefill, training) ----------------
     if need_backward:
@@ -402,6 +404,8 @@ def _prefill_modes(C, W, torch, dev, to_dev, time_it, w):
     o = torch.empty((w.B, w.N, w.H_q, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
     bm, bn = C.cowa_fwd_block_sizes(w.d)
+    fws = torch.empty(C.cowa_fwd_workspace_size(w.B, w.N, w.H_kv, w.d), dtype=torch.uint8,
+                      device=dev)
     G = w.H_q // w.H_kv
     t = np.arange(w.N)
     res = {}
@@ -409,7 +413,7 @@ def _prefill_modes(C, W, torch, dev, to_dev, time_it, w):
         p = C.make_pattern(w.N, w.sink, w.window, 0, w.h_kv_global, 0, mode)
         rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, w.N, w.H_kv, bm, bn)]
         ms = time_it(lambda: C.cowa_fwd(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
-                                        1.0 / np.sqrt(w.d)), 5)
+                                        1.0 / np.sqrt(w.d), workspace=fws), 5)
         if mode == 0:
             pairs = sum(int(visible_counts(t, g, w.sink, w.window, w.stated_band).sum())
                         for g in range(w.H_kv))
@@ -448,6 +452,8 @@ def ablation_8k(C, W, torch, dev, to_dev, time_it):
     o = torch.empty((w.B, w.N, w.H_q, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
     bm, bn = C.cowa_fwd_block_sizes(w.d)
+    fws = torch.empty(C.cowa_fwd_workspace_size(w.B, w.N, w.H_kv, w.d), dtype=torch.uint8,
+                      device=dev)
     G = w.H_q // w.H_kv
     t = np.arange(w.N)
     out = []
@@ -455,7 +461,7 @@ def ablation_8k(C, W, torch, dev, to_dev, time_it):
         p = C.make_pattern(w.N, w.sink, w.window, 0, w.h_kv_global, 0, 0, m)
         rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, w.N, w.H_kv, bm, bn)]
         ms = time_it(lambda: C.cowa_fwd(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
-                                        1.0 / np.sqrt(w.d)), 5)
+                                        1.0 / np.sqrt(w.d), workspace=fws), 5)
         pairs = sum(int(visible_counts(t, g % m, w.sink, w.window, w.stated_band).sum())
                     for g in range(w.H_kv))
         flops = 4.0 * w.d * G * w.B * pairs
@@ -477,8 +483,10 @@ def varlen_prefill(C, W, torch, dev, time_it):
     p = C.make_pattern(w.n_ctx, w.sink, w.window, 0, w.h_kv_global, 0, 0)
     bm, bn = C.cowa_fwd_block_sizes(w.d)
     rp, col, fl = [torch.from_numpy(a).to(dev) for a in C.cowa_plan(p, max_len, w.H_kv, bm, bn)]
+    fws = torch.empty(C.cowa_fwd_workspace_size(len(lens), max_len, w.H_kv, w.d),
+                      dtype=torch.uint8, device=dev)
     ms = time_it(lambda: C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse,
-                                           cu, max_len, 1.0 / np.sqrt(w.d)), 5)
+                                           cu, max_len, 1.0 / np.sqrt(w.d), workspace=fws), 5)
     band = C.cowa_band_length(p)
     G = w.H_q // w.H_kv
     pairs = 0

@@ -50,8 +50,8 @@
  *    windowed caches, new tokens) must be 16-byte aligned and every batch,
  *    token and head stride a multiple of 16 bytes (8 bf16 or 4 fp32
  *    elements); otherwise COWA_ERR_INVALID_ARG before any launch.  The
- *    forward also needs 64 token strides of K and of V below 2^30 elements
- *    (COWA_ERR_UNSUPPORTED otherwise).
+ *    forward also needs 64 token strides of K below 2^30 elements and
+ *    d * (N rounded up to 64) below 2^30 (COWA_ERR_UNSUPPORTED otherwise).
  *  - The library is thread-safe.  Its only state is per-thread caches of
  *    plan sizes and launch-order choices per shape, which change no result.
  */
@@ -69,7 +69,7 @@ typedef enum {
   COWA_OK = 0,
   COWA_ERR_INVALID_ARG = 1,   /* a size, pointer or pattern field is invalid */
   COWA_ERR_UNSUPPORTED = 2,   /* valid but not compiled (head dim, tile shape, group size) */
-  COWA_ERR_WORKSPACE = 3,     /* decode or backward workspace missing, misaligned or too small */
+  COWA_ERR_WORKSPACE = 3,     /* workspace missing, misaligned or too small */
   COWA_ERR_PLAN_MISMATCH = 4, /* plan size does not match pattern/shape/tile */
   COWA_ERR_HIP = 5,           /* a HIP launch failed */
   COWA_ERR_CAPACITY = 6,      /* caller's plan buffers are too small */
@@ -170,6 +170,13 @@ cowa_status cowa_plan(const cowa_pattern* p, int32_t n, int32_t h_kv_local,
  *  d           64 or 128; H_q % H_kv_local == 0;
  *              kv_head_offset + H_kv_local <= h_kv_global
  *  softmax_scale  > 0 (usually 1/sqrt(d))
+ *  workspace   caller-owned device memory, 256-byte aligned, at least
+ *              cowa_fwd_workspace_size(B, N, H_kv_local, d) bytes, else
+ *              COWA_ERR_WORKSPACE.  The call writes V into it head-dim-major
+ *              (one row of keys per head dimension) before the attention
+ *              kernel reads it; its contents need no initialisation and are
+ *              overwritten by every call.  Calls that overlap in time need
+ *              separate workspaces.
  * Arithmetic: bf16 inputs, fp32 accumulation and softmax; P is rounded to
  * bf16 before the P.V product. */
 cowa_status cowa_fwd(const cowa_pattern* p,
@@ -178,7 +185,16 @@ cowa_status cowa_fwd(const cowa_pattern* p,
                      const void* q, const void* k, const void* v,
                      void* o, int32_t o_dtype, float* lse,
                      int32_t B, int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
-                     const int64_t strides[12], float softmax_scale, void* stream);
+                     const int64_t strides[12], float softmax_scale,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of cowa_fwd for B sequences of N keys (cowa_fwd_varlen:
+ * B = n_seqs, N = max_seqlen) with H_kv_local KV heads of dimension d:
+ * B * H_kv_local * d * (N rounded up to 64) bf16 values, rounded up to 256
+ * bytes.  COWA_ERR_INVALID_ARG for a non-positive size or a null bytes,
+ * COWA_ERR_UNSUPPORTED for d other than 64 and 128. */
+cowa_status cowa_fwd_workspace_size(int32_t B, int32_t N, int32_t H_kv_local, int32_t d,
+                                    size_t* bytes);
 
 /* Packed ("varlen") prefill: n_seqs sequences of different lengths back to
  * back in one launch, a second workload shape of the same operator (used in
@@ -192,14 +208,17 @@ cowa_status cowa_fwd(const cowa_pattern* p,
  *  plan           cowa_plan for n = max_seqlen (one plan serves every length:
  *                 visibility depends on positions only)
  *  lse            fp32 [H_q, total_tokens]
- *  strides        element strides (t, h) of q, k, v, o (8). */
+ *  strides        element strides (t, h) of q, k, v, o (8)
+ *  workspace      as for cowa_fwd, at least
+ *                 cowa_fwd_workspace_size(n_seqs, max_seqlen, H_kv_local, d). */
 cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_row_ptr,
                             const int32_t* d_col, const uint8_t* d_flags, int64_t nnz,
                             int32_t block_m, int32_t block_n, const void* q, const void* k,
                             const void* v, void* o, int32_t o_dtype, float* lse,
                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t max_seqlen,
                             int32_t total_tokens, int32_t H_q, int32_t H_kv_local, int32_t d,
-                            const int64_t strides[8], float softmax_scale, void* stream);
+                            const int64_t strides[8], float softmax_scale,
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- cowa_decode: one query token per sequence --------------------------
  * Sequence b's new token sits at position t_b = cache_seqlens[b] - 1 (its own

@@ -36,7 +36,8 @@ EXPORTED = ("cowa_status_str", "cowa_band_length", "cowa_fwd_block_sizes", "cowa
             "cowa_bwd_block_sizes", "cowa_plan_kv_size", "cowa_plan_kv",
             "cowa_bwd_workspace_size", "cowa_bwd", "cowa_bwd_varlen", "cowa_kv_window_rows",
             "cowa_kv_window_fill", "cowa_kv_window_append", "cowa_decode_window",
-            "cowa_fwd_varlen", "cowa_visible_ranges", "cowa_decode_noalloc")
+            "cowa_fwd_varlen", "cowa_visible_ranges", "cowa_decode_noalloc",
+            "cowa_fwd_workspace_size")
 
 
 class CowaError(RuntimeError):
@@ -89,7 +90,9 @@ def load():
     lib.cowa_plan.argtypes = [pat, i32, i32, i32, i32, vp, vp, vp, i64]
     lib.cowa_fwd.restype = ctypes.c_int
     lib.cowa_fwd.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp,
-                             i32, i32, i32, i32, i32, P(i64), f32, vp]
+                             i32, i32, i32, i32, i32, P(i64), f32, vp, ctypes.c_size_t, vp]
+    lib.cowa_fwd_workspace_size.restype = ctypes.c_int
+    lib.cowa_fwd_workspace_size.argtypes = [i32, i32, i32, i32, P(ctypes.c_size_t)]
     lib.cowa_decode_workspace_size.restype = ctypes.c_int
     lib.cowa_decode_workspace_size.argtypes = [pat, i32, i32, i32, i32, i32, P(ctypes.c_size_t)]
     lib.cowa_decode.restype = ctypes.c_int
@@ -129,7 +132,8 @@ def load():
     lib.cowa_visible_ranges.argtypes = [pat, i32, i32, P(i32), P(i32)]
     lib.cowa_fwd_varlen.restype = ctypes.c_int
     lib.cowa_fwd_varlen.argtypes = [pat, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp,
-                                    i32, i32, i32, i32, i32, i32, P(i64), f32, vp]
+                                    i32, i32, i32, i32, i32, i32, P(i64), f32, vp,
+                                    ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -214,9 +218,29 @@ def _o_dtype(o):
     raise TypeError("o must be bfloat16 or float32")
 
 
+def cowa_fwd_workspace_size(B: int, N: int, H_kv_local: int, d: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().cowa_fwd_workspace_size(B, N, H_kv_local, d, ctypes.byref(n)),
+           "cowa_fwd_workspace_size")
+    return n.value
+
+
+def _fwd_workspace(workspace, B, N, Hkv, d, device):
+    """(pointer, bytes) of the caller's workspace, or of a new uint8 device
+    tensor of the required size when workspace is None (callers that must not
+    allocate per call, such as graph capture, pass their own)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(cowa_fwd_workspace_size(B, N, Hkv, d), dtype=torch.uint8,
+                                device=device)
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def cowa_fwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
-             q, k, v, o, lse, softmax_scale: float, stream=None):
-    """Prefill forward.  q/o [B,N,H_q,d], k/v [B,N,H_kv,d] (bf16), lse [B,H_q,N] fp32."""
+             q, k, v, o, lse, softmax_scale: float, stream=None, workspace=None):
+    """Prefill forward.  q/o [B,N,H_q,d], k/v [B,N,H_kv,d] (bf16), lse [B,H_q,N] fp32;
+    workspace: a device tensor of at least cowa_fwd_workspace_size(B, N, H_kv, d)
+    bytes, or None for a new one."""
     import torch
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda:
@@ -231,10 +255,11 @@ def cowa_fwd(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block
         raise ValueError("o must be [B, N, H_q, d] and lse [B, H_q, N]")
     strides = (ctypes.c_int64 * 12)(*(_strides(q, 3) + _strides(k, 3) + _strides(v, 3)
                                       + _strides(o, 3)))
+    ws, ws_ptr, ws_bytes = _fwd_workspace(workspace, B, N, Hkv, d, q.device)
     st = load().cowa_fwd(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
                          nnz, block_m, block_n, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                          o.data_ptr(), _o_dtype(o), lse.data_ptr(), B, N, Hq, Hkv, d,
-                         strides, float(softmax_scale), _stream_ptr(stream))
+                         strides, float(softmax_scale), ws_ptr, ws_bytes, _stream_ptr(stream))
     _check(st, "cowa_fwd")
 
 
@@ -473,9 +498,10 @@ def cowa_decode_window(p: cowa_pattern, q, k_win, v_win, cache_seqlens, o, lse, 
 
 def cowa_fwd_varlen(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int, block_n: int,
                     q, k, v, o, lse, cu_seqlens, max_seqlen: int, softmax_scale: float,
-                    stream=None):
+                    stream=None, workspace=None):
     """Packed prefill: q/o [T, H_q, d], k/v [T, H_kv, d], lse [H_q, T], cu_seqlens
-    int32 [n_seqs + 1] on the device; the plan is built for n = max_seqlen."""
+    int32 [n_seqs + 1] on the device; the plan is built for n = max_seqlen;
+    workspace as for cowa_fwd with B = n_seqs, N = max_seqlen."""
     import torch
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda:
@@ -490,10 +516,12 @@ def cowa_fwd_varlen(p: cowa_pattern, row_ptr, col, flags, nnz: int, block_m: int
         raise ValueError("o must be [T, H_q, d] and lse [H_q, T]")
     strides = (ctypes.c_int64 * 8)(*(_strides(q, 2) + _strides(k, 2) + _strides(v, 2)
                                      + _strides(o, 2)))
+    ws, ws_ptr, ws_bytes = _fwd_workspace(workspace, cu_seqlens.numel() - 1, max_seqlen, Hkv,
+                                          d, q.device)
     st = load().cowa_fwd_varlen(ctypes.byref(p), row_ptr.data_ptr(), col.data_ptr(),
                                 flags.data_ptr(), nnz, block_m, block_n, q.data_ptr(),
                                 k.data_ptr(), v.data_ptr(), o.data_ptr(), _o_dtype(o),
                                 lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
                                 max_seqlen, T, Hq, Hkv, d, strides, float(softmax_scale),
-                                _stream_ptr(stream))
+                                ws_ptr, ws_bytes, _stream_ptr(stream))
     _check(st, "cowa_fwd_varlen")

@@ -267,7 +267,8 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
                             void* o, int32_t o_dtype, float* lse, int32_t B, int32_t N,
                             int32_t H_q, int32_t H_kv_local, int32_t d,
                             const int64_t strides[12], float softmax_scale,
-                            const int32_t* cu_seqlens, int32_t total_tokens, void* stream) {
+                            const int32_t* cu_seqlens, int32_t total_tokens, void* workspace,
+                            size_t ws_bytes, void* stream) {
   cowa_status st = validate_pattern(p, H_kv_local);
   if (st != COWA_OK) return st;
   if (!d_row_ptr || !d_col || !d_flags || !q || !k || !v || !o || !lse || !strides)
@@ -281,9 +282,14 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
     return COWA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
   if (block_m != kFwdBlockM || block_n != kFwdBlockN) return COWA_ERR_UNSUPPORTED;
-  // per-lane byte offsets inside one K/V tile are 31-bit (buffer loads)
-  if ((int64_t)block_n * strides[4] >= (1LL << 30) || (int64_t)block_n * strides[7] >= (1LL << 30))
+  // per-lane byte offsets inside one K tile, and inside one tile of the
+  // head-dim-major V copy (d rows of npad keys), are 31-bit (buffer loads)
+  const int64_t npad = (N + (int64_t)kFwdBlockN - 1) / kFwdBlockN * kFwdBlockN;
+  if ((int64_t)block_n * strides[4] >= (1LL << 30) || (int64_t)d * npad * 2 >= (1LL << 31))
     return COWA_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+      ws_bytes < fwd_workspace_bytes(B, N, H_kv_local, d))
+    return COWA_ERR_WORKSPACE;
   const int64_t nqt = (N + block_m - 1) / block_m;
   if (!grid_fits((int64_t)B * nqt * H_q, (int64_t)B * H_q)) return COWA_ERR_UNSUPPORTED;
   int64_t want = 0;
@@ -326,9 +332,19 @@ static cowa_status fwd_impl(const cowa_pattern* p, const int32_t* d_row_ptr, con
     if (st != COWA_OK) return st;
     fp.xcd_chunk = gc.fwd;
   }
+  fp.vt = static_cast<uint16_t*>(workspace);
+  fp.npad = (int32_t)npad;
   fp.scale = softmax_scale;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
   return launch_fwd(fp, d, o_dtype == COWA_DTYPE_F32, stream) == 0 ? COWA_OK : COWA_ERR_HIP;
+}
+
+extern "C" cowa_status cowa_fwd_workspace_size(int32_t B, int32_t N, int32_t H_kv_local,
+                                               int32_t d, size_t* bytes) {
+  if (!bytes || B < 1 || N < 1 || H_kv_local < 1) return COWA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return COWA_ERR_UNSUPPORTED;
+  *bytes = fwd_workspace_bytes(B, N, H_kv_local, d);
+  return COWA_OK;
 }
 
 extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
@@ -336,9 +352,11 @@ extern "C" cowa_status cowa_fwd(const cowa_pattern* p, const int32_t* d_row_ptr,
                                 int32_t block_m, int32_t block_n, const void* q, const void* k,
                                 const void* v, void* o, int32_t o_dtype, float* lse, int32_t B,
                                 int32_t N, int32_t H_q, int32_t H_kv_local, int32_t d,
-                                const int64_t strides[12], float softmax_scale, void* stream) {
+                                const int64_t strides[12], float softmax_scale,
+                                void* workspace, size_t ws_bytes, void* stream) {
   return fwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, q, k, v, o, o_dtype, lse,
-                  B, N, H_q, H_kv_local, d, strides, softmax_scale, nullptr, 0, stream);
+                  B, N, H_q, H_kv_local, d, strides, softmax_scale, nullptr, 0, workspace,
+                  ws_bytes, stream);
 }
 
 extern "C" cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_row_ptr,
@@ -348,7 +366,8 @@ extern "C" cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_r
                                        float* lse, const int32_t* cu_seqlens, int32_t n_seqs,
                                        int32_t max_seqlen, int32_t total_tokens, int32_t H_q,
                                        int32_t H_kv_local, int32_t d, const int64_t strides[8],
-                                       float softmax_scale, void* stream) {
+                                       float softmax_scale, void* workspace, size_t ws_bytes,
+                                       void* stream) {
   if (!cu_seqlens || !strides) return COWA_ERR_INVALID_ARG;
   if (n_seqs < 1 || total_tokens < 1 || max_seqlen < 1) return COWA_ERR_INVALID_ARG;
   // token rows: (t, h) strides; the per-sequence offset comes from cu_seqlens
@@ -356,7 +375,7 @@ extern "C" cowa_status cowa_fwd_varlen(const cowa_pattern* p, const int32_t* d_r
                             0, strides[4], strides[5], 0, strides[6], strides[7]};
   return fwd_impl(p, d_row_ptr, d_col, d_flags, nnz, block_m, block_n, q, k, v, o, o_dtype, lse,
                   n_seqs, max_seqlen, H_q, H_kv_local, d, full, softmax_scale, cu_seqlens,
-                  total_tokens, stream);
+                  total_tokens, workspace, ws_bytes, stream);
 }
 
 extern "C" cowa_status cowa_decode_workspace_size(const cowa_pattern* p, int32_t B, int32_t H_q,

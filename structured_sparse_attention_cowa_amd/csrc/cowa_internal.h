@@ -40,6 +40,13 @@ inline int64_t xcd_grid(int64_t total, int32_t chunk) {
 constexpr int kFwdBlockM = 256;
 constexpr int kFwdBlockN = 64;
 
+// Bytes of the forward's workspace: V head-dim-major for B sequences of up to
+// N keys (N rounded up to kFwdBlockN), 256-byte multiple.
+inline size_t fwd_workspace_bytes(int64_t B, int64_t N, int64_t H_kv, int64_t d) {
+  const int64_t npad = (N + kFwdBlockN - 1) / kFwdBlockN * kFwdBlockN;
+  return ((size_t)(B * H_kv * d * npad * 2) + 255) / 256 * 256;
+}
+
 // Decode: largest visible-key chunk one workgroup handles, and the largest
 // GQA group size compiled.
 constexpr int kDecodeChunkMax = 768;
@@ -75,6 +82,12 @@ struct FwdParams {
   const int32_t* cu_seqlens;
   int32_t total_tokens;
   int32_t xcd_chunk;  // workgroup order: chunks of this many go to one XCD (0: launch_fwd's default)
+  // workspace: V head-dim-major, [B][H_kv][d][npad] bf16 (B = sequences when
+  // packed), the keys of each 16-key group stored in the order the P operand
+  // takes them (tr16_position), zero past each sequence's end; written by the
+  // transpose kernel of launch_fwd before the forward kernel reads it
+  uint16_t* vt;
+  int32_t npad;  // N (the longest sequence when packed) rounded up to 64
   float scale;       // softmax scale (natural-log domain)
   float scale_log2;  // scale * log2(e)
 };

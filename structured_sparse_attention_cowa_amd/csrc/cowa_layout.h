@@ -89,6 +89,19 @@ COWA_HD void tr_offsets(int32_t lane, int32_t (&off)[2][D / 32]) {
     }
 }
 
+// Head-dim-major tiles (one row per head dim, 64 positions = 8 chunks of 8):
+// the MFMA operand reads take 16 consecutive rows at one chunk, which this
+// swizzle spreads over all banks (whether the LDS serves 128 or 256 bytes per
+// cycle).  It repeats every 64 rows.
+COWA_HD int32_t swz_tr8(int32_t row) { return (row ^ (row >> 3)) & 7; }
+
+// Storage position of key r inside its group of 16 in a head-dim-major copy:
+// bits 2 and 3 swapped, so that the 8 positions a lane reads as one 16-byte
+// chunk (k index 8 * (lane / 32) + m of the 32x32x16 MFMA) are the keys the
+// probability accumulator gives that lane: 8 (m / 4) + 4 (lane / 32) + m % 4.
+// The map is its own inverse.
+COWA_HD int32_t tr16_position(int32_t r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
 // Direct global -> LDS loads: the loading lanes of a tile, in order, fill
 // 16-byte LDS chunk positions P = 0, 1, ...; position P holds row P / (D / 8),
 // column chunk (P % (D / 8)) ^ swz_both(row), i.e. the global chunk read by

@@ -22,11 +22,15 @@
 // layout (lane half 0 holds keys 0-3 and 8-11, half 1 keys 4-7 and 12-15).
 //
 // K and V tiles go from HBM straight into LDS (16 bytes per lane, no
-// register staging), row-major with the 16-byte chunks of each row XOR-
-// swizzled by a function of the row so that the reads below are free of
-// bank conflicts.  K feeds the first product with 16-byte reads; V feeds
-// the second through the gfx950 transposing read (ds_read_b64_tr_b16), which
-// hands each lane four keys of one head dimension.
+// register staging), with the 16-byte chunks of each row XOR-swizzled by a
+// function of the row so that the reads below are free of bank conflicts.
+// K tiles are row-major (key rows) and feed the first product with 16-byte
+// reads.  V is read from a head-dim-major copy that a transpose kernel writes
+// into the workspace first (one row per head dim, the keys of each 16-key
+// group in the order the P^T operand takes them), so each operand of the
+// second product is also one 16-byte read: the LDS serves the transposing
+// read (ds_read_b64_tr_b16) that the row-major V would need at well under
+// half the rate of 16-byte reads.
 #include <hip/hip_runtime.h>
 
 #include "cowa_internal.h"
@@ -48,17 +52,55 @@ constexpr int NTHREADS = 64 * NWAVES;
 // maximum is used for the sum and for the output).
 constexpr float RESCALE_LOG2 = 8.0f;
 
-// LDS swizzles (16-byte chunk index XOR a function of the row), chosen so
-// that the reads below hit distinct banks whether the LDS serves 128 or 256
-// bytes per cycle.  K: 16 consecutive rows read one column chunk.  V: the
-// transposing read takes 4 consecutive keys x 2-4 adjacent chunks.
+// K-tile swizzle (16-byte chunk index XOR a function of the row), chosen so
+// that 16 consecutive rows reading one column chunk hit distinct banks
+// whether the LDS serves 128 or 256 bytes per cycle.  (V tiles use swz_tr8.)
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
   return D == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
 }
+
+// V head-dim-major into the workspace: grid (npad / 64, H_kv, B), one
+// workgroup per 64 keys of one (sequence, KV head), through LDS.  Keys past
+// the sequence's end are written as zeros (a plan built for the longest
+// sequence may list such tiles: their keys are masked, and a zero value keeps
+// the masked products exactly zero).
 template <int D>
-__device__ __forceinline__ int vswz(int key) {
-  return D == 128 ? ((((key & 3) << 2) ^ ((key & 3) << 1)) & 14) : (2 * (key & 3));
+__global__ __launch_bounds__(256) void cowa_fwd_vt_kernel(FwdParams p) {
+  constexpr int CH = D / 8;  // 16-byte chunks per key row
+  __shared__ __attribute__((aligned(16))) uint16_t tile[BN][D + 8];
+  const int tid = threadIdx.x;
+  const int k0 = blockIdx.x * BN;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  int n = p.N;
+  int64_t base = (int64_t)b * p.vs_b + (int64_t)h * p.vs_h;
+  if (p.cu_seqlens) {
+    const int start = p.cu_seqlens[b];
+    n = min(p.cu_seqlens[b + 1] - start, p.N);
+    base = (int64_t)start * p.vs_t + (int64_t)h * p.vs_h;
+  }
+  for (int c = tid; c < BN * CH; c += 256) {
+    const int r = c / CH, k = c % CH;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (k0 + r < n) w = ldg16(p.v + base + (int64_t)(k0 + r) * p.vs_t + 8 * k);
+    *reinterpret_cast<u32x4*>(&tile[r][8 * k]) = w;
+  }
+  __syncthreads();
+  // row dd of the copy: 8 chunks of 8 positions, position q holding key
+  // k0 + tr16_position(q)
+  uint16_t* dst = p.vt + ((int64_t)b * p.Hkv + h) * D * p.npad + k0;
+  for (int c = tid; c < D * 8; c += 256) {
+    const int dd = c >> 3, k = c & 7;
+    unsigned w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q0 = 8 * k + 2 * j;
+      w[j] = (unsigned)tile[tr16_position(q0)][dd] |
+             ((unsigned)tile[tr16_position(q0 + 1)][dd] << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + (int64_t)dd * p.npad + 8 * k) = u32x4{w[0], w[1], w[2], w[3]};
+  }
 }
 
 template <int D, bool OF32>
@@ -101,7 +143,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 
   // this sequence's length and the offsets of its rows
   int N = p.N;
-  int64_t qb = (int64_t)b * p.qs_b, kb = (int64_t)b * p.ks_b, vb = (int64_t)b * p.vs_b;
+  int64_t qb = (int64_t)b * p.qs_b, kb = (int64_t)b * p.ks_b;
   int64_t ob = (int64_t)b * p.os_b, lse_base = ((int64_t)b * p.Hq + hq) * p.N;
   if (p.cu_seqlens) {
     const int start = p.cu_seqlens[b];
@@ -109,7 +151,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     if (qi * BM >= N) return;  // the whole workgroup: this tile is past the sequence
     qb = (int64_t)start * p.qs_t;
     kb = (int64_t)start * p.ks_t;
-    vb = (int64_t)start * p.vs_t;
     ob = (int64_t)start * p.os_t;
     lse_base = (int64_t)hq * p.total_tokens + start;
   }
@@ -141,21 +182,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   const int e0 = p.row_ptr[row];
   const int e1 = p.row_ptr[row + 1];
   const uint16_t* kbase = p.k + kb + (int64_t)h * p.ks_h;
-  const uint16_t* vbase = p.v + vb + (int64_t)h * p.vs_h;
+  // V: the head-dim-major copy (rows d of npad keys) of this sequence and head
+  const uint16_t* vbase = p.vt + ((int64_t)b * p.Hkv + h) * D * p.npad;
 
   // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
   // holds row P / CPR, column chunk (P % CPR) ^ swizzle(row).  Per-lane
   // offsets inside a tile are fixed; the tile base is uniform.
   auto ld_row = [&](int i) { return ((wave * LOADS + i) * 64 + lane) / CPR; };
-  auto ld_col = [&](int i, bool is_v) {
-    const int r = ld_row(i);
-    return ((lane % CPR) ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 8;
-  };
-  int ld_koff[LOADS], ld_voff[LOADS];
+  auto ld_col = [&](int i) { return ((lane % CPR) ^ kswz<D>(ld_row(i))) * 8; };
+  int ld_koff[LOADS];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i, false);
-    ld_voff[i] = (int)(ld_row(i) * p.vs_t) + ld_col(i, true);
+  for (int i = 0; i < LOADS; ++i) ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i);
+  // V tiles: D rows (head dims) of 64 keys, 8 chunks of 8 keys per row;
+  // position P = (wave * VLOADS + i) * 64 + lane of the LDS tile holds row
+  // P / 8, chunk (P % 8) ^ swz_tr8(row)
+  constexpr int VLOADS = D * 8 / 64 / NWAVES;
+  static_assert(VLOADS >= 1, "every wavefront loads part of each tile");
+  int ld_voff[VLOADS];
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int P = (wave * VLOADS + i) * 64 + lane;
+    ld_voff[i] = (P >> 3) * p.npad + ((P & 7) ^ swz_tr8(P >> 3)) * 8;
   }
   // Loads of one K (or V) tile into LDS buffer dst, through a buffer
   // resource based at the tile (buffer_load ... lds).  Keys past N (ragged
@@ -166,8 +213,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   // flight; with the global form it waits for every outstanding LDS read at
   // each of them.  Byte offsets inside a tile stay below 2^31 (checked on the
   // host).
-  auto load_tile = [&](const uint16_t* base, int64_t stride, const int* off, bool is_v, int kj,
-                       uint16_t* dst) {
+  auto load_k = [&](const uint16_t* base, int64_t stride, const int* off, int kj,
+                    uint16_t* dst) {
     const int key0 = kj * BN;
     const __amdgpu_buffer_rsrc_t rs = lds_rsrc(base + (int64_t)key0 * stride);
     if (key0 + BN <= N) {
@@ -178,10 +225,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       for (int i = 0; i < LOADS; ++i) {
         int key = key0 + ld_row(i);
         key = key < N ? key : N - 1;
-        buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + ld_col(i, is_v)) * 2),
+        buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + ld_col(i)) * 2),
                   dst + (wave * LOADS + i) * 512);
       }
     }
+  };
+  // V tile kj: every key of the copy exists (zero past the sequence's end)
+  auto load_v = [&](int kj, uint16_t* dst) {
+    const __amdgpu_buffer_rsrc_t rs = lds_rsrc(vbase + (int64_t)kj * BN);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) buf2lds16(rs, ld_voff[i] * 2, dst + (wave * VLOADS + i) * 512);
   };
 
   // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl.
@@ -195,21 +248,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       k_off[blk][ks] = (blk == 1 && D == 128)
                            ? k_off[0][ks] + 32 * D
                            : (32 * blk + l32) * D + (((2 * ks + hl) ^ kswz<D>(32 * blk + l32)) * 8);
-  // V transposed-read offsets (second product, A operand): for 16-key step st,
-  // d block db and half ri, lane reads key 16*st + 8*ri + 4*hl + (lane&15)/4 at
-  // dims 32*db + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
-  const int r16 = lane & 15;
-  const int gi = (lane >> 4) & 1;
-  // (the swizzle depends on key mod 4, so half ri = 1 is 8 rows further)
-  int v_off[2][ND];
+  // V read offsets (second product, A operand): for 16-key step st and d
+  // block db the lane reads row 32*db + l32, chunk 2*st + hl, i.e. the 8 keys
+  // (in the copy's order) that its P operand holds.  The swizzle repeats
+  // every 64 rows, so blocks 2, 3 read 64 rows further than 0, 1.
+  int v_off[ND][4];
 #pragma unroll
-  for (int ri = 0; ri < 2; ++ri)
+  for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int key = 8 * ri + 4 * hl + (r16 >> 2);
-      const int d = 32 * db + 16 * gi + 4 * (r16 & 3);
-      v_off[ri][db] = ri == 1 ? v_off[0][db] + 8 * D
-                              : key * D + (((d >> 3) ^ vswz<D>(key)) * 8) + (d & 7);
+    for (int st = 0; st < 4; ++st) {
+      const int dr = 32 * db + l32;
+      v_off[db][st] = db >= 2 ? v_off[db - 2][st] + 64 * BN
+                              : dr * BN + (((2 * st + hl) ^ swz_tr8(dr)) * 8);
     }
 
   // Plan entries travel 64 at a time, one per lane (tile index with the
@@ -246,9 +296,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   if (e0 < e1) {
     c_cur = entry(e0);
     c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
-    load_tile(kbase, p.ks_t, ld_koff, false, c_cur & 0x7fffffff, K0);
-    load_tile(vbase, p.vs_t, ld_voff, true, c_cur & 0x7fffffff, V0);
-    if (e0 + 1 < e1) load_tile(kbase, p.ks_t, ld_koff, false, c_n1 & 0x7fffffff, K1);
+    load_k(kbase, p.ks_t, ld_koff, c_cur & 0x7fffffff, K0);
+    load_v(c_cur & 0x7fffffff, V0);
+    if (e0 + 1 < e1) load_k(kbase, p.ks_t, ld_koff, c_n1 & 0x7fffffff, K1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(K0, s_first);
@@ -271,9 +321,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pchunk = plan_chunk(pbase);
       }
       c_n2 = entry(e + 2);
-      load_tile(kbase, p.ks_t, ld_koff, false, c_n2 & 0x7fffffff, Kw);
+      load_k(kbase, p.ks_t, ld_koff, c_n2 & 0x7fffffff, Kw);
     }
-    if (has_next) load_tile(vbase, p.vs_t, ld_voff, true, c_n1 & 0x7fffffff, Vw);
+    if (has_next) load_v(c_n1 & 0x7fffffff, Vw);
 
     if (__builtin_expect(!full, 0)) {
       // register i of block blk holds key kj*64 + 4 hl + o
@@ -328,10 +378,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       const bf16x8 bv = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const i16x4 lo = lds_read_tr(Vs + st * 16 * D + v_off[0][db]);
-        const i16x4 hi = lds_read_tr(Vs + st * 16 * D + v_off[1][db]);
-        const i16x4 a8[2] = {lo, hi};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + v_off[db][st]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
@@ -348,7 +395,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
     c_cur = c_n1;
@@ -401,6 +448,11 @@ int launch_fwd(const FwdParams& p_in, int d, int o_f32, void* stream) {
   const dim3 grid((unsigned)xcd_grid(per_qi * p.nqt, p.xcd_chunk));
   const dim3 block(NTHREADS);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 vt_grid((unsigned)(p.npad / BN), (unsigned)p.Hkv, (unsigned)p.B);
+  if (d == 128)
+    hipLaunchKernelGGL(cowa_fwd_vt_kernel<128>, vt_grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(cowa_fwd_vt_kernel<64>, vt_grid, dim3(256), 0, s, p);
   if (d == 128) {
     if (o_f32)
       hipLaunchKernelGGL((cowa_fwd_kernel<128, true>), grid, block, 0, s, p);

@@ -78,11 +78,13 @@ class Prefill:
         odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
         self.o = torch.empty((B, N, Hq, d), dtype=odt, device="cuda")
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(C.cowa_fwd_workspace_size(B, N, Hkv, d), dtype=torch.uint8,
+                              device="cuda")
         self.scale = 1.0 / np.sqrt(d)
 
     def run(self, stream=None):
         C.cowa_fwd(self.pattern, self.rp, self.col, self.fl, self.nnz, self.bm, self.bn,
-                   self.q, self.k, self.v, self.o, self.lse, self.scale, stream)
+                   self.q, self.k, self.v, self.o, self.lse, self.scale, stream, self.ws)
 
     def result(self):
         import torch

@@ -81,6 +81,8 @@ def test_graph_replays_match_eager_varlen(lib):
                       for a in C.cowa_plan_kv(p, max_len, Hkv, bmk, bnk)]
     ws = torch.empty(C.cowa_bwd_workspace_size(p, len(lens), Hq, Hkv, max_len),
                      dtype=torch.uint8, device="cuda")
+    fws = torch.empty(C.cowa_fwd_workspace_size(len(lens), max_len, Hkv, d), dtype=torch.uint8,
+                      device="cuda")
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
     dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
@@ -90,7 +92,7 @@ def test_graph_replays_match_eager_varlen(lib):
 
     def work():
         C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse, cu, max_len,
-                          scale)
+                          scale, workspace=fws)
         C.cowa_bwd_varlen(p, rp, col, fl, col.numel(), bm, bn, rpk, colk, flk, colk.numel(),
                           bmk, bnk, q, k, v, o, do, lse, dq, dk, dv, cu, max_len, scale, ws)
 

@@ -114,3 +114,40 @@ def test_varlen_32k_workload_sampled(lib):
         torch.cuda.synchronize()
         assert torch.equal(o1[0], o[a:b]), f"seq {i}"
         assert torch.equal(l1[0], lse[:, a:b]), f"seq {i}"
+
+
+def test_forward_workspace_contents_do_not_matter(lib):
+    """The forward writes the head-dim-major V copy into its workspace before
+    reading it, including zeros past every sequence's end: a workspace full of
+    NaN bytes, or one left from a longer batch, gives the same bits."""
+    import torch
+    lens = np.array([300, 1000, 77], np.int64)
+    Hq, Hkv, d = 4, 2, 128
+    T, max_len = int(lens.sum()), int(lens.max())
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    x = W.random_prefill(811, 1, T, Hq, Hkv, d)
+    q, k, v = bits_to_dev(x.q_bits[0]), bits_to_dev(x.k_bits[0]), bits_to_dev(x.v_bits[0])
+    p = C.make_pattern(max_len, 8, 64, 0, 4, 0)
+    bm, bn = C.cowa_fwd_block_sizes(d)
+    rp, col, fl = [torch.from_numpy(a).cuda() for a in C.cowa_plan(p, max_len, Hkv, bm, bn)]
+    scale = 1.0 / np.sqrt(d)
+
+    def run(ws):
+        o = torch.empty((T, Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+        C.cowa_fwd_varlen(p, rp, col, fl, col.numel(), bm, bn, q, k, v, o, lse, cu, max_len,
+                          scale, workspace=ws)
+        torch.cuda.synchronize()
+        return o, lse
+
+    need = C.cowa_fwd_workspace_size(len(lens), max_len, Hkv, d)
+    o0, l0 = run(torch.zeros(need, dtype=torch.uint8, device="cuda"))
+    assert torch.isfinite(o0).all() and torch.isfinite(l0).all()
+    nan_ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o1, l1 = run(nan_ws)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    # the same bytes after a batch of longer sequences (a larger workspace)
+    big = torch.full((C.cowa_fwd_workspace_size(3, 4096, Hkv, d),), 0x7F, dtype=torch.uint8,
+                     device="cuda")
+    o2, l2 = run(big)
+    assert torch.equal(o0, o2) and torch.equal(l0, l2)

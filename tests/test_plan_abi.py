@@ -143,8 +143,12 @@ def test_fwd_block_sizes(lib):
     assert e.value.status == C.COWA_ERR_UNSUPPORTED
 
 
+FAKE_WS = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced
+BIG_WS = 1 << 40
+
+
 def _fwd_raw(lib, cp, nnz=None, bm=None, bn=None, B=1, N=256, Hq=4, Hkv=2, d=128, scale=0.1,
-             o_dtype=0, null=None, strides=None):
+             o_dtype=0, null=None, strides=None, ws=FAKE_WS, ws_bytes=BIG_WS):
     """Calls cowa_fwd with fake (never dereferenced) device pointers: every
     case here must be rejected on the host before any launch."""
     fake = ctypes.c_void_p(0x1000)
@@ -160,7 +164,7 @@ def _fwd_raw(lib, cp, nnz=None, bm=None, bn=None, B=1, N=256, Hq=4, Hkv=2, d=128
     arr = (ctypes.c_int64 * 12)(*s)
     return lib.cowa_fwd(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, bm, bn,
                         ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], o_dtype, ptrs["lse"],
-                        B, N, Hq, Hkv, d, arr, scale, None)
+                        B, N, Hq, Hkv, d, arr, scale, ws, ws_bytes, None)
 
 
 def test_fwd_host_validation(lib):
@@ -198,6 +202,22 @@ def test_fwd_host_validation(lib):
     nnz_other = C.cowa_plan_size(cpw, 4096, 2, fbm, fbn)
     assert nnz_other != C.cowa_plan_size(cp4, 4096, 2, fbm, fbn)
     assert _fwd_raw(lib, cp4, nnz=nnz_other, N=4096) == E.COWA_ERR_PLAN_MISMATCH
+    # workspace: V head-dim-major, B * H_kv * d * (N rounded up to 64) bf16,
+    # 256-byte aligned
+    need = C.cowa_fwd_workspace_size(1, 256, 2, 128)
+    assert need == 2 * 128 * 256 * 2
+    assert C.cowa_fwd_workspace_size(3, 130, 2, 64) == (3 * 2 * 64 * 192 * 2 + 255) // 256 * 256
+    assert _fwd_raw(lib, cp, ws=None) == E.COWA_ERR_WORKSPACE
+    assert _fwd_raw(lib, cp, ws=ctypes.c_void_p(0x100080)) == E.COWA_ERR_WORKSPACE
+    assert _fwd_raw(lib, cp, ws_bytes=need - 1) == E.COWA_ERR_WORKSPACE
+    assert _fwd_raw(lib, cp, ws_bytes=need, nnz=3) == E.COWA_ERR_PLAN_MISMATCH
+    for bad in ((0, 1, 1, 128), (1, 0, 1, 128), (1, 1, 0, 128)):
+        with pytest.raises(C.CowaError) as e:
+            C.cowa_fwd_workspace_size(*bad)
+        assert e.value.status == E.COWA_ERR_INVALID_ARG
+    with pytest.raises(C.CowaError) as e:
+        C.cowa_fwd_workspace_size(1, 1, 1, 96)
+    assert e.value.status == E.COWA_ERR_UNSUPPORTED
 
 
 def test_misaligned_pointers_are_rejected(lib):
@@ -211,7 +231,8 @@ def test_misaligned_pointers_are_rejected(lib):
         t = [good] * 4
         t[which] = bad
         assert lib.cowa_fwd(ctypes.byref(cp), good, good, good, nnz, fbm, fbn, *t, 0, good, 1, 256,
-                            4, 2, 128, arr, 0.1, None) == C.COWA_ERR_INVALID_ARG, which
+                            4, 2, 128, arr, 0.1, FAKE_WS, BIG_WS, None) == \
+            C.COWA_ERR_INVALID_ARG, which
     cpd, _ = pat(n_ctx=4096, sink=16, window=128, h_kv_global=4)
     ws = C.cowa_decode_workspace_size(cpd, 2, 8, 4, 128, 4096)
     arr10 = (ctypes.c_int64 * 10)(*([8] * 10))
@@ -294,7 +315,7 @@ def _varlen_raw(lib, cp, nnz=None, n_seqs=3, max_seqlen=300, total=700, Hq=4, Hk
     return lib.cowa_fwd_varlen(ctypes.byref(cp), ptrs["rp"], ptrs["col"], ptrs["fl"], nnz, fbm,
                                fbn, ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], 1, ptrs["lse"],
                                ptrs["cu"], n_seqs, max_seqlen, total, Hq, Hkv, d, arr, scale,
-                               None)
+                               FAKE_WS, BIG_WS, None)
 
 
 def test_fwd_varlen_host_validation(lib):
