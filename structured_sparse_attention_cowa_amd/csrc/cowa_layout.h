@@ -102,6 +102,29 @@ COWA_HD int32_t swz_tr8(int32_t row) { return (row ^ (row >> 3)) & 7; }
 // The map is its own inverse.
 COWA_HD int32_t tr16_position(int32_t r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Operand reads from a head-dim-major tile (rows of 64 positions): for
+// 16-position step st and head-dim block db, the lane reads row
+// 32 db + lane % 32, chunk 2 st + lane / 32.  Element offsets off[db][st];
+// the swizzle repeats every 64 rows, so blocks 2, 3 are blocks 0, 1 plus a
+// constant (which the compiler folds into the read's offset field).
+template <int D>
+COWA_HD void hdm_read_offsets(int32_t lane, int32_t (&off)[D / 32][4]) {
+  const int32_t l32 = lane & 31, hl = lane >> 5;
+  COWA_UNROLL
+  for (int db = 0; db < D / 32; ++db)
+    COWA_UNROLL
+    for (int st = 0; st < 4; ++st) {
+      const int32_t row = 32 * db + l32;
+      off[db][st] = db >= 2 ? off[db - 2][st] + 64 * 64
+                            : row * 64 + (((2 * st + hl) ^ swz_tr8(row)) * 8);
+    }
+}
+
+// Direct loads of a head-dim-major tile: LDS chunk position P holds row
+// P / 8 and the tile's chunk (P % 8) ^ swz_tr8(P / 8) of that row.
+COWA_HD int32_t hdm_load_row(int32_t P) { return P >> 3; }
+COWA_HD int32_t hdm_load_chunk(int32_t P) { return (P & 7) ^ swz_tr8(P >> 3); }
+
 // Direct global -> LDS loads: the loading lanes of a tile, in order, fill
 // 16-byte LDS chunk positions P = 0, 1, ...; position P holds row P / (D / 8),
 // column chunk (P % (D / 8)) ^ swz_both(row), i.e. the global chunk read by

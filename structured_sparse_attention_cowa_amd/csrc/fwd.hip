@@ -193,16 +193,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   int ld_koff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i);
-  // V tiles: D rows (head dims) of 64 keys, 8 chunks of 8 keys per row;
-  // position P = (wave * VLOADS + i) * 64 + lane of the LDS tile holds row
-  // P / 8, chunk (P % 8) ^ swz_tr8(row)
+  // V tiles: D rows (head dims) of 64 keys, 8 chunks of 8 keys per row,
+  // filled in LDS chunk positions P = (wave * VLOADS + i) * 64 + lane
   constexpr int VLOADS = D * 8 / 64 / NWAVES;
   static_assert(VLOADS >= 1, "every wavefront loads part of each tile");
   int ld_voff[VLOADS];
 #pragma unroll
   for (int i = 0; i < VLOADS; ++i) {
     const int P = (wave * VLOADS + i) * 64 + lane;
-    ld_voff[i] = (P >> 3) * p.npad + ((P & 7) ^ swz_tr8(P >> 3)) * 8;
+    ld_voff[i] = hdm_load_row(P) * p.npad + hdm_load_chunk(P) * 8;
   }
   // Loads of one K (or V) tile into LDS buffer dst, through a buffer
   // resource based at the tile (buffer_load ... lds).  Keys past N (ragged
@@ -250,17 +249,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                            : (32 * blk + l32) * D + (((2 * ks + hl) ^ kswz<D>(32 * blk + l32)) * 8);
   // V read offsets (second product, A operand): for 16-key step st and d
   // block db the lane reads row 32*db + l32, chunk 2*st + hl, i.e. the 8 keys
-  // (in the copy's order) that its P operand holds.  The swizzle repeats
-  // every 64 rows, so blocks 2, 3 read 64 rows further than 0, 1.
+  // (in the copy's order) that its P operand holds
+  static_assert(BN == 64, "head-dim-major tiles hold 64 keys per row");
   int v_off[ND][4];
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int dr = 32 * db + l32;
-      v_off[db][st] = db >= 2 ? v_off[db - 2][st] + 64 * BN
-                              : dr * BN + (((2 * st + hl) ^ swz_tr8(dr)) * 8);
-    }
+  hdm_read_offsets<D>(lane, v_off);
 
   // Plan entries travel 64 at a time, one per lane (tile index with the
   // full-tile flag in bit 31), and are picked out with readlane.

@@ -71,6 +71,24 @@ void shim_tr_offsets(int32_t d, int32_t lane, int32_t* out) {
 }
 
 int32_t shim_load_row(int32_t d, int32_t P) { return d == 128 ? load_row<128>(P) : load_row<64>(P); }
+
+// Head-dim-major tiles: swizzle, position order inside 16-key groups, and
+// one lane's operand-read offsets out[db * 4 + st].
+int32_t shim_swz_tr8(int32_t row) { return swz_tr8(row); }
+int32_t shim_tr16_position(int32_t r) { return tr16_position(r); }
+void shim_hdm_read_offsets(int32_t d, int32_t lane, int32_t* out) {
+  if (d == 128) {
+    int32_t off[4][4];
+    hdm_read_offsets<128>(lane, off);
+    for (int i = 0; i < 16; ++i) out[i] = off[i / 4][i % 4];
+  } else {
+    int32_t off[2][4];
+    hdm_read_offsets<64>(lane, off);
+    for (int i = 0; i < 8; ++i) out[i] = off[i / 4][i % 4];
+  }
+}
+int32_t shim_hdm_load_row(int32_t P) { return hdm_load_row(P); }
+int32_t shim_hdm_load_chunk(int32_t P) { return hdm_load_chunk(P); }
 int32_t shim_load_col(int32_t d, int32_t P) { return d == 128 ? load_col<128>(P) : load_col<64>(P); }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ def load():
     lib.shim_load_row.argtypes = [i32, i32]
     lib.shim_load_col.restype = i32
     lib.shim_load_col.argtypes = [i32, i32]
+    for name in ("shim_swz_tr8", "shim_tr16_position", "shim_hdm_load_row", "shim_hdm_load_chunk"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [i32]
+    lib.shim_hdm_read_offsets.restype = None
+    lib.shim_hdm_read_offsets.argtypes = [i32, i32, P32]
     _lib = lib
     return lib
 
