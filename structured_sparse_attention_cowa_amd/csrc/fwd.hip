@@ -10,7 +10,11 @@
 // tiles the plan marks partial are masked.
 //
 // Workgroup = 8 wavefronts = 256 query rows of one (batch, query head), so
-// every K/V tile staged in LDS serves 256 query rows.
+// every K/V tile staged in LDS serves 256 query rows.  Wavefront w runs on
+// SIMD w % 4, so each SIMD holds one wavefront of waves 0-3 (group A) and one
+// of waves 4-7 (group B); the two groups run the pipeline half a step apart
+// (below), so that on every SIMD one of them issues MFMAs while the other
+// runs its softmax.
 // Each wavefront owns 32 query rows and works in the transposed frame:
 //   S^T (32 keys x 32 queries) = K (32 x d) . Q^T (d x 32)     [MFMA 32x32x16]
 //   O^T (d x 32 queries)      += V^T (d x 64) . P^T (64 x 32)   [MFMA 32x32x16]
@@ -108,8 +112,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void cowa_fwd_kernel(FwdParams p) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
   constexpr int TILE = BN * D;                // bf16 elements per K or V tile
-  constexpr int LOADS = BN * CPR / 64 / NWAVES;  // direct loads per wave per tile
-  static_assert(LOADS >= 1, "every wavefront loads part of each tile");
   constexpr int ND = D / 32;                  // 32-wide d blocks of O^T
   constexpr int NK = D / 16;                  // 16-deep k steps of Q.K
 
@@ -185,55 +187,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
   // V: the head-dim-major copy (rows d of npad keys) of this sequence and head
   const uint16_t* vbase = p.vt + ((int64_t)b * p.Hkv + h) * D * p.npad;
 
-  // Direct-load geometry: LDS chunk position P = (wave*LOADS + i)*64 + lane
-  // holds row P / CPR, column chunk (P % CPR) ^ swizzle(row).  Per-lane
-  // offsets inside a tile are fixed; the tile base is uniform.
-  auto ld_row = [&](int i) { return ((wave * LOADS + i) * 64 + lane) / CPR; };
+  // Group A streams whole tiles: LDS chunk position P = (wave * LOADS_A + i)
+  // * 64 + lane of a K tile holds row P / CPR, column chunk (P % CPR) ^
+  // kswz(row); of a V tile, row hdm_load_row(P), chunk hdm_load_chunk(P).
+  // Keys past N (ragged last tile) are clamped to N - 1: they only occur in
+  // tiles the plan marks partial, where they are masked (probability exactly
+  // 0).  The loads are buffer loads to LDS (buffer_load ... lds) through a
+  // resource based at the tile: with the global form of the direct-to-LDS
+  // load the compiler waits for every outstanding LDS read at each one.
+  // Byte offsets inside a tile stay below 2^31 (checked on the host).
+  constexpr int HALF = NWAVES / 2;
+  constexpr int LOADS_A = BN * CPR / 64 / HALF;   // K tile loads per group-A lane
+  constexpr int VLOADS_A = D * 8 / 64 / HALF;     // V tile loads per group-A lane
+  static_assert(LOADS_A >= 1 && VLOADS_A >= 1, "group A loads whole tiles");
+  const bool grpB = wave >= HALF;
+  const int wa = grpB ? 0 : wave;
+  auto ld_row = [&](int i) { return ((wa * LOADS_A + i) * 64 + lane) / CPR; };
   auto ld_col = [&](int i) { return ((lane % CPR) ^ kswz<D>(ld_row(i))) * 8; };
-  int ld_koff[LOADS];
+  int ld_koff[LOADS_A];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i);
-  // V tiles: D rows (head dims) of 64 keys, 8 chunks of 8 keys per row,
-  // filled in LDS chunk positions P = (wave * VLOADS + i) * 64 + lane
-  constexpr int VLOADS = D * 8 / 64 / NWAVES;
-  static_assert(VLOADS >= 1, "every wavefront loads part of each tile");
-  int ld_voff[VLOADS];
+  for (int i = 0; i < LOADS_A; ++i) ld_koff[i] = (int)(ld_row(i) * p.ks_t) + ld_col(i);
+  int ld_voff[VLOADS_A];
 #pragma unroll
-  for (int i = 0; i < VLOADS; ++i) {
-    const int P = (wave * VLOADS + i) * 64 + lane;
+  for (int i = 0; i < VLOADS_A; ++i) {
+    const int P = (wa * VLOADS_A + i) * 64 + lane;
     ld_voff[i] = hdm_load_row(P) * p.npad + hdm_load_chunk(P) * 8;
   }
-  // Loads of one K (or V) tile into LDS buffer dst, through a buffer
-  // resource based at the tile (buffer_load ... lds).  Keys past N (ragged
-  // last tile) are clamped to N - 1: they only occur in tiles the plan marks
-  // partial, where they are masked (probability exactly 0).  The buffer form
-  // of the direct-to-LDS load (not the global one) lets the compiler count
-  // the LDS reads that feed the MFMAs precisely while tile loads are in
-  // flight; with the global form it waits for every outstanding LDS read at
-  // each of them.  Byte offsets inside a tile stay below 2^31 (checked on the
-  // host).
   auto load_k = [&](const uint16_t* base, int64_t stride, const int* off, int kj,
                     uint16_t* dst) {
     const int key0 = kj * BN;
     const __amdgpu_buffer_rsrc_t rs = lds_rsrc(base + (int64_t)key0 * stride);
     if (key0 + BN <= N) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) buf2lds16(rs, off[i] * 2, dst + (wave * LOADS + i) * 512);
+      for (int i = 0; i < LOADS_A; ++i) buf2lds16(rs, off[i] * 2, dst + (wa * LOADS_A + i) * 512);
     } else {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
+      for (int i = 0; i < LOADS_A; ++i) {
         int key = key0 + ld_row(i);
         key = key < N ? key : N - 1;
         buf2lds16(rs, (int)(((int64_t)(key - key0) * stride + ld_col(i)) * 2),
-                  dst + (wave * LOADS + i) * 512);
+                  dst + (wa * LOADS_A + i) * 512);
       }
     }
   };
-  // V tile kj: every key of the copy exists (zero past the sequence's end)
   auto load_v = [&](int kj, uint16_t* dst) {
     const __amdgpu_buffer_rsrc_t rs = lds_rsrc(vbase + (int64_t)kj * BN);
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) buf2lds16(rs, ld_voff[i] * 2, dst + (wave * VLOADS + i) * 512);
+    for (int i = 0; i < VLOADS_A; ++i)
+      buf2lds16(rs, ld_voff[i] * 2, dst + (wa * VLOADS_A + i) * 512);
   };
 
   // K read offsets (first product, A operand): row 32*blk + l32, chunk 2*ks + hl.
@@ -279,62 +280,50 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     }
   };
 
-  // Pipeline: iteration e holds S(e) in registers, reads K(e+1) and V(e) from
-  // LDS, and streams K(e+2) and V(e+1) into the buffers freed last iteration.
-  // The MFMAs of S(e+1) are independent of the softmax of S(e), so they
-  // overlap it.
-  f32x16 s_first[2];
-  int c_cur = 0, c_n1 = 0;  // plan entries of tiles e and e + 1
+  // Every wave runs the same sequence of half-steps, M(e0-1), V(e0), M(e0),
+  // V(e0+1), ..., M(e1-1), separated by workgroup barriers: M(e-1) computes
+  // S(e) = K(e) Q^T and O^T += V(e-1)^T P(e-1) (MFMA work), V(e) masks S(e),
+  // updates the row statistics and makes P(e) (VALU work).  Group B runs one
+  // half-step behind group A (one extra barrier before its loop, A one after
+  // its last product), so on every SIMD one wave issues MFMAs while the other
+  // runs the softmax.  Tile e sits in buffers e mod 2 (relative to e0); group
+  // A's M(e-1) streams K(e+1) and V(e) into the buffers both groups finished
+  // reading two half-steps before, and the barrier after V(e) waits for them.
+  f32x16 s[2];
+  unsigned pk[2][8];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk[blk][i] = 0u;
+  int c_cur = 0;  // plan entry of tile e
   if (e0 < e1) {
     c_cur = entry(e0);
-    c_n1 = e0 + 1 < e1 ? entry(e0 + 1) : 0;
-    load_k(kbase, p.ks_t, ld_koff, c_cur & 0x7fffffff, K0);
-    load_v(c_cur & 0x7fffffff, V0);
-    if (e0 + 1 < e1) load_k(kbase, p.ks_t, ld_koff, c_n1 & 0x7fffffff, K1);
+    if (!grpB) load_k(kbase, p.ks_t, ld_koff, c_cur & 0x7fffffff, K0);
+    // V1 starts as zeros: M(e0-1) multiplies it by P = 0
+    for (int i = tid; i < TILE / 8; i += NTHREADS)
+      *reinterpret_cast<u32x4*>(V1 + 8 * i) = u32x4{0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    qk(K0, s_first);
-    // every wave has read K(e0) before its buffer is refilled
-    __syncthreads();
+    if (grpB) __builtin_amdgcn_s_barrier();
   }
 
-  // One pipeline step for tile e; s_cur holds S(e), s_nxt receives S(e+1).
-  // Reads K(e+1) from Kr and V(e) from Vr; K(e+2) streams into Kw, V(e+1) into Vw.
-  auto step = [&](int e, f32x16* s_cur, f32x16* s_nxt, const uint16_t* Kr, const uint16_t* Vr,
-                  uint16_t* Kw, uint16_t* Vw) {
-    const int kj = c_cur & 0x7fffffff;
-    const bool full = c_cur < 0;
-    const bool has_next = e + 1 < e1;
-    // plan entry of tile e + 2 (the chunk moves on when e + 2 leaves it)
-    int c_n2 = 0;
-    if (e + 2 < e1) {
-      if (e + 2 - pbase == 64) {
-        pbase += 64;
-        pchunk = plan_chunk(pbase);
-      }
-      c_n2 = entry(e + 2);
-      load_k(kbase, p.ks_t, ld_koff, c_n2 & 0x7fffffff, Kw);
-    }
-    if (has_next) load_v(c_n1 & 0x7fffffff, Vw);
-
+  auto valu_half = [&](int c) {
+    const int kj = c & 0x7fffffff;
+    const bool full = c < 0;
     if (__builtin_expect(!full, 0)) {
-      // register i of block blk holds key kj*64 + 4 hl + o
       const uint64_t vis = row_visible_bits(hp, q_row, kj * BN + 4 * hl);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          s_cur[blk][i] = keep_if(s_cur[blk][i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
+          s[blk][i] = keep_if(s[blk][i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
     }
-
     float mt = NEG_INF;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s_cur[blk][i]);
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
     mt = pair_max(mt);
-    // raise the reference maximum only where it grew past the threshold
-    // (always on a row's first visible key: m_run = -inf gives +inf)
     const bool grow = (mt - m_run) * p.scale_log2 > RESCALE_LOG2;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run;
@@ -346,22 +335,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       for (int i = 0; i < ND; ++i) acc[i] *= alpha;
     }
     const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
-
-    // ---- one basic block: S(e+1) MFMAs, softmax of S(e), P.V MFMAs ----
-    // (unconditional so that the scheduler can interleave it with the
-    // softmax; on a row's last tile it reads a stale buffer and is unused)
-    qk(Kr, s_nxt);
-    unsigned pk[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][2 * i], p.scale_log2, -mb));
-        const float c = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][2 * i + 1], p.scale_log2, -mb));
-        pk[blk][i] = pack_bf16(a, c);
-        l_run += a + c;
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i], p.scale_log2, -mb));
+        const float c2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i + 1], p.scale_log2, -mb));
+        pk[blk][i] = pack_bf16(a, c2);
+        l_run += a + c2;
       }
-    const uint16_t* Vs = Vr;
+  };
+  auto pv = [&](const uint16_t* Vr) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int blk = st >> 1;
@@ -370,37 +354,53 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       const bf16x8 bv = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + v_off[db][st]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vr + v_off[db][st]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[db], 0, 0, 0);
       }
     }
-    // interleave: MFMAs of S(e+1) with the softmax VALU of S(e), then the
-    // P.V MFMAs with their transposed V reads
+  };
+  // iteration e: K(e) in Kc, V(e-1) in Vp; group A streams K(e+1) into Kn
+  // and V(e) into Vc
+  auto iter = [&](int e, const uint16_t* Kc, uint16_t* Kn, uint16_t* Vc, const uint16_t* Vp) {
+    int c_n1 = 0;
+    if (e + 1 < e1) {
+      if (e + 1 - pbase == 64) {
+        pbase += 64;
+        pchunk = plan_chunk(pbase);
+      }
+      c_n1 = entry(e + 1);
+    }
+    if (!grpB) {
+      if (e + 1 < e1) load_k(kbase, p.ks_t, ld_koff, c_n1 & 0x7fffffff, Kn);
+      load_v(c_cur & 0x7fffffff, Vc);
+    }
+    // M(e-1): 32 MFMAs, each fed by one 16-byte LDS read issued six reads
+    // ahead
+    qk(Kc, s);
+    pv(Vp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
+    // (no wait here: group A's tile loads stay in flight across this barrier)
+    __builtin_amdgcn_s_barrier();
+    // V(e)
+    valu_half(c_cur);
     c_cur = c_n1;
-    c_n1 = c_n2;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  // unrolled by two so the two S register sets and the buffers alternate
-  // without copies or run-time buffer selection
-  f32x16 s_alt[2];
   for (int e = e0; e < e1; e += 2) {
-    step(e, s_first, s_alt, K1, V0, K0, V1);
-    if (e + 1 < e1) step(e + 1, s_alt, s_first, K0, V1, K1, V0);
+    iter(e, K0, K1, V0, V1);
+    if (e + 1 < e1) iter(e + 1, K1, K0, V1, V0);
+  }
+  // M(e1-1): the last tile's P.V product (no further tile)
+  if (e0 < e1) {
+    pv(((e1 - 1 - e0) & 1) ? V1 : V0);
+    if (!grpB) __builtin_amdgcn_s_barrier();
   }
 
   const float l_tot = pair_sum(l_run);
