@@ -344,6 +344,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         pk[blk][i] = pack_bf16(a, c2);
         l_run += a + c2;
       }
+    // P is made in this half: the compiler may not sink this arithmetic past
+    // the barrier into the MFMA half that consumes it
+    asm volatile("" : "+v"(pk[0][0]), "+v"(pk[0][1]), "+v"(pk[0][2]), "+v"(pk[0][3]),
+                 "+v"(pk[0][4]), "+v"(pk[0][5]), "+v"(pk[0][6]), "+v"(pk[0][7]));
+    asm volatile("" : "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(pk[1][2]), "+v"(pk[1][3]),
+                 "+v"(pk[1][4]), "+v"(pk[1][5]), "+v"(pk[1][6]), "+v"(pk[1][7]));
   };
   auto pv = [&](const uint16_t* Vr) {
 #pragma unroll
@@ -385,6 +391,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    // S is complete in this half (not sunk into the VALU half that reads it)
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     // (no wait here: group A's tile loads stay in flight across this barrier)
     __builtin_amdgcn_s_barrier();
     // V(e)
