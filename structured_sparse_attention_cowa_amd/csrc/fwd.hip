@@ -393,7 +393,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     }
     // S is complete in this half (not sunk into the VALU half that reads it)
     asm volatile("" : "+v"(s[0]), "+v"(s[1]));
-    // (no wait here: group A's tile loads stay in flight across this barrier)
+    // Every LDS read of this half is issued before the barrier: group A's
+    // next loads overwrite Vp after it.  (No wait here: group A's tile loads
+    // stay in flight across this barrier.)
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     // V(e)
     valu_half(c_cur);
