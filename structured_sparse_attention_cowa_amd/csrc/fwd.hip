@@ -53,8 +53,12 @@ constexpr int NTHREADS = 64 * NWAVES;
 // The running maximum is only raised when a row's maximum grows by more than
 // 2^RESCALE_LOG2 in probability terms; until then the stale maximum is kept
 // and probabilities may reach 2^RESCALE_LOG2 (exact: the same reference
-// maximum is used for the sum and for the output).
-constexpr float RESCALE_LOG2 = 8.0f;
+// maximum is used for the sum and for the output).  At 2^16 the sums stay far
+// inside fp32 range (at most 2^16 per key) and bf16 keeps its relative
+// precision, while a row's reference is rarely raised after its first tile,
+// even with a few large-norm keys.
+constexpr float RESCALE_LOG2 = 16.0f;
+constexpr float RESCALE_BOUND = 65536.0f;  // 2^RESCALE_LOG2
 
 // K-tile swizzle (16-byte chunk index XOR a function of the row), chosen so
 // that 16 consecutive rows reading one column chunk hit distinct banks
@@ -318,32 +322,57 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
         for (int i = 0; i < 16; ++i)
           s[blk][i] = keep_if(s[blk][i], vis, 32 * blk + 8 * (i >> 2) + (i & 3));
     }
-    float mt = NEG_INF;
+    // Probabilities against the current reference maximum first.  If each
+    // lane's sum (which bounds every one of its terms) stays at or below
+    // 2^RESCALE_LOG2, no key of the row exceeds the reference by more than
+    // the threshold, the reference stays, and the row maximum is not needed.
+    // Otherwise, and on a row's first step (no reference yet), the wavefront
+    // takes the maximum, raises the reference where it grew, and makes the
+    // probabilities again.
+    float lp = 0.f;
+    {
+      const float mb = m_run * p.scale_log2;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
-    mt = pair_max(mt);
-    const bool grow = (mt - m_run) * p.scale_log2 > RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mt : m_run;
-      const float alpha =
-          m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+        for (int i = 0; i < 8; ++i) {
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i], p.scale_log2, -mb));
+          const float c2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i + 1], p.scale_log2, -mb));
+          pk[blk][i] = pack_bf16(a, c2);
+          lp += a + c2;
+        }
     }
-    const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
+    const bool slow = !(lp <= RESCALE_BOUND) || m_run == NEG_INF;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(slow) != 0, 0)) {
+      float mt = NEG_INF;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i], p.scale_log2, -mb));
-        const float c2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i + 1], p.scale_log2, -mb));
-        pk[blk][i] = pack_bf16(a, c2);
-        l_run += a + c2;
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[blk][i]);
+      mt = pair_max(mt);
+      const bool grow = (mt - m_run) * p.scale_log2 > RESCALE_LOG2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha =
+            m_run == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) acc[i] *= alpha;
       }
+      const float mb = m_run == NEG_INF ? 0.f : m_run * p.scale_log2;
+      lp = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i], p.scale_log2, -mb));
+          const float c2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][2 * i + 1], p.scale_log2, -mb));
+          pk[blk][i] = pack_bf16(a, c2);
+          lp += a + c2;
+        }
+    }
+    l_run += lp;
     // P is made in this half: the compiler may not sink this arithmetic past
     // the barrier into the MFMA half that consumes it
     asm volatile("" : "+v"(pk[0][0]), "+v"(pk[0][1]), "+v"(pk[0][2]), "+v"(pk[0][3]),
