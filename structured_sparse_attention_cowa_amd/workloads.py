@@ -169,6 +169,22 @@ def random_prefill(seed, B, N, H_q, H_kv, d, scale_q=1.0):
     return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
 
 
+def hot_key_prefill(seed, B, N, H_q, H_kv, d, hot):
+    """Inputs whose scores jump late in a row: every query gets the common
+    direction u = (1, ..., 1) / sqrt(d) added with weight 2, and the keys at
+    the positions in `hot` (a dict position -> gain) are replaced by gain * u,
+    so their scores are about 2 * gain above the typical N(0, d) score spread.
+    Rows see the hot keys only once their tiles come up, after ordinary ones."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = np.full(d, 1.0 / np.sqrt(d), dtype=np.float32)
+    q = rng.standard_normal((B, N, H_q, d), dtype=np.float32) + np.float32(2.0) * u
+    k = rng.standard_normal((B, N, H_kv, d), dtype=np.float32)
+    v = rng.standard_normal((B, N, H_kv, d), dtype=np.float32)
+    for j, gain in hot.items():
+        k[:, j, :, :] = np.float32(gain) * u
+    return PrefillInputs(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v))
+
+
 # Position codes: value rows that identify their key position.  With a zero
 # query every visible score is equal, so an output row is the mean of the
 # value rows of exactly the visible keys; with 0/1 codes (exact in bf16) the

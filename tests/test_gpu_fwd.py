@@ -56,6 +56,17 @@ def test_edge_shapes(lib, N, S, Wd, H, off, Hq, Hkv, d):
     _full_compare(x, S, Wd, H, off, what=f"edge N={N}")
 
 
+@pytest.mark.parametrize("S,d", [(16, 128), (0, 128), (16, 64)])
+def test_scores_jumping_late_in_a_row(lib, S, d):
+    # keys whose scores exceed everything before them by about 2.5, 10, 40
+    # and 160 log2 units, met by rows after ordinary tiles: the running
+    # maximum must stay (small jumps) or be raised mid-row with the
+    # accumulated terms rescaled (large ones), on every path of the kernel
+    hot = {300: 10.0, 700: 40.0, 1200: 160.0, 1800: 640.0}
+    x = W.hot_key_prefill(31 + S + d, 1, 2048, 4, 2, d, hot)
+    _full_compare(x, S, 256, 2, what=f"hot keys S={S} d={d}")
+
+
 def test_dense_reduction_equals_causal_mode(lib):
     # S + W >= N makes CoWA dense causal: both modes must agree closely
     x = W.random_prefill(31, 1, 700, 4, 2, 128)
