@@ -185,13 +185,16 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
   // ---- phase A: scores ----
   {
     const int quad = lane / LPA;   // key slot of this lane
-    const int part = lane % LPA;   // dims [part*DPL, (part+1)*DPL)
+    // dims 8 part + 8 LPA i + (0..7), i < NVA: each 16-byte load of the
+    // eight lanes of a key covers one whole 128-byte line of its row (two
+    // loads of adjacent 16-byte pieces per lane read 10% slower)
+    const int part = lane % LPA;
     u32x4 qr[G][NVA];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const uint16_t* qp = p.q + (int64_t)b * p.qs_b + (int64_t)(h * G + hh) * p.qs_h + part * DPL;
+      const uint16_t* qp = p.q + (int64_t)b * p.qs_b + (int64_t)(h * G + hh) * p.qs_h + part * 8;
 #pragma unroll
-      for (int i = 0; i < NVA; ++i) qr[hh][i] = ldg16(qp + 8 * i);
+      for (int i = 0; i < NVA; ++i) qr[hh][i] = ldg16(qp + 8 * LPA * i);
     }
     float mx[G];
 #pragma unroll
@@ -204,9 +207,9 @@ __global__ __launch_bounds__(NTHREADS) void cowa_decode_split(DecodeParams p) {
         const int kk = base + NWAVES * KPA * u;
         if (kk < cnt) {
           const int key = sg.row(v0 + kk);
-          const uint16_t* kp = kbase + (int64_t)key * p.ks_t + part * DPL;
+          const uint16_t* kp = kbase + (int64_t)key * p.ks_t + part * 8;
 #pragma unroll
-          for (int i = 0; i < NVA; ++i) kr[u][i] = ldg16_stream(kp + 8 * i);
+          for (int i = 0; i < NVA; ++i) kr[u][i] = ldg16_stream(kp + 8 * LPA * i);
         }
       }
 #pragma unroll
