@@ -103,14 +103,25 @@ typedef struct {
   int32_t n_bands;
 } cowa_pattern;
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage).  A library utility:
+ * the pages define no error model. */
 const char* cowa_status_str(cowa_status s);
 
-/* Resolved band width L of a pattern, or -1 if the pattern is invalid. */
+/* Resolved band width L of a pattern, or -1 if the pattern is invalid.  L is
+ * the length of each KV head's long-range interval: the pages split the
+ * history beyond the local window into one non-overlapping interval per KV
+ * head ("Splitting long-range windows across KV heads beats duplicating them
+ * at lower cost", mechanism paragraph) without a formula; this library's
+ * formula is the one at the top of this header: the pattern's own band if it
+ * sets one, else ceil((n_ctx - W) / h_kv_global) (0 when n_ctx <= W), and 0
+ * in COWA_MODE_SINK_LOCAL. */
 int32_t cowa_band_length(const cowa_pattern* p);
 
 /* Tile shape (block_m query rows x block_n keys) that cowa_fwd requires for
- * head dim d; COWA_ERR_UNSUPPORTED if d is not compiled (64 and 128 are). */
+ * head dim d; COWA_ERR_UNSUPPORTED if d is not compiled (64 and 128 are).  A
+ * property of these kernels, not of the method: the visible-tile lists the
+ * pages describe as position arithmetic (news page, efficiency paragraph) are
+ * built for this tile shape. */
 cowa_status cowa_fwd_block_sizes(int32_t d, int32_t* block_m, int32_t* block_n);
 
 /* ---- cowa_visible_ranges: the keys one query row sees (host only) -------
