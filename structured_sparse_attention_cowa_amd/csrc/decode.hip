@@ -57,7 +57,6 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int DPP_XOR1 = 0xb1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4e;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8 lanes
-constexpr int DPP_ROR8 = 0x128;        // rotate by 8 within 16 lanes (= xor 8)
 
 // Sum over aligned groups of 8 lanes, result on every lane of the group.
 __device__ __forceinline__ float sum8(float a) {
@@ -66,14 +65,6 @@ __device__ __forceinline__ float sum8(float a) {
   return a + dpp<DPP_HALF_MIRROR>(a);
 }
 
-// Maximum over the wavefront of values that are uniform within 8-lane groups.
-__device__ __forceinline__ float wave_max_of_groups8(float m) {
-  m = fmaxf(m, dpp<DPP_ROR8>(m));
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
-                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
-                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
-}
 
 struct Segs {
   int lo0, n0, lo1, n1, lo2, n2;
