@@ -414,8 +414,9 @@ static cowa_status decode_impl(const cowa_pattern* p, const void* q, const void*
   const int32_t G = H_q / H_kv_local;
   if (G > kDecodeMaxGroup) return COWA_ERR_UNSUPPORTED;
   const DecodeGeometry geo = decode_geometry(p, B, H_q, H_kv_local, d, n_max);
-  if ((int64_t)geo.n_splits > 0x7fffffffLL || B > 65535 || H_kv_local > 65535)
-    return COWA_ERR_UNSUPPORTED;
+  // grid (splits, H_kv_local, B): splits are at most ceil(n_max / 64); the
+  // other two dimensions are limited to 65535
+  if (B > 65535 || H_kv_local > 65535) return COWA_ERR_UNSUPPORTED;
   if (noalloc) {
     // the library's own scratch (cowa_decode_noalloc): no caller workspace
     if (geo.total_bytes > COWA_DECODE_SCRATCH_BYTES) return COWA_ERR_SCRATCH_LIMIT;
