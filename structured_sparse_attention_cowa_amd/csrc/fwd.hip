@@ -271,7 +271,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
     return __builtin_amdgcn_readlane(pchunk, e - pbase);
   };
 
-  // S^T = K Q^T for the 64 keys of the K tile in buffer kb
+  // S^T = K Q^T for the 64 keys of the K tile in buffer Ks
   auto qk = [&](const uint16_t* Ks, f32x16* s) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
