@@ -11,7 +11,7 @@
 //   dV_j = sum_{t, heads of the group} P_tj dO_t
 // P is recomputed from the forward's LSE, so no probability matrix is stored.
 //
-// Three kernels on the caller's stream:
+// Four kernels on the caller's stream:
 //   delta  D_t and LSE in base-2 units into the workspace (rows padded to a
 //          multiple of 64; padding rows get LSE = +inf, so P = 0 there);
 //   dQ     one workgroup per (batch, query head, 256-row query tile), the
@@ -28,7 +28,7 @@
 //          atomics.  Key tiles holding sink keys are seen by every query
 //          tile; their step lists are cut into parts that run as separate
 //          workgroups writing fp32 partials, which a last kernel sums in a
-//          fixed order, so the result stays deterministic.
+//          fixed order (the fourth kernel), so the result stays deterministic.
 // Tiles stream from HBM straight into LDS (16 bytes per lane), double
 // buffered, with one swizzle that serves both the plain and the transposing
 // reads without bank conflicts.
